@@ -1,0 +1,254 @@
+"""Pins of the oracle's page scores and 16-slot selection (CPU only).
+
+Each test checks the oracle against something other than itself: a hand-worked
+example, exact rational brute force, a heap selection, closed forms (one-hot
+queries, zero queries, identical pages) and invariants of the method.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests import pins
+
+
+def _hand_pool(ex):
+    num = ex["num_blocks"]
+    pool = np.zeros((num, 128, 68), dtype=np.uint8)
+    pool[:, :, 64:] = 127
+    bt = ex["block_table_logical_to_physical"]
+    for tk in ex["tokens"]:
+        phys = bt[tk["page"]]
+        t, d = tk["token"], tk["dim"]
+        b = d // 2
+        if d % 2 == 0:
+            pool[phys, t, b] = (pool[phys, t, b] & 0xF0) | tk["code"]
+        else:
+            pool[phys, t, b] = (pool[phys, t, b] & 0x0F) | (tk["code"] << 4)
+        pool[phys, t, 64 + d // 32] = tk["scale_byte"]
+    return pool.reshape(num, 8704), np.array([bt], dtype=np.int32)
+
+
+def test_hand_worked_example():
+    ex = pins.hand_example()
+    pool, bt = _hand_pool(ex)
+    H = len(ex["q_onehot_dims_per_head"])
+    q = np.zeros((1, H, 128), dtype=np.uint8)
+    for h, d in enumerate(ex["q_onehot_dims_per_head"]):
+        q[0, h, d] = 0x38                      # E4M3 1.0
+    out, scores, L = oracle.oracle_decode(q, pool, bt, np.array([ex["seq_len"]]),
+                                          ex["query_len"])
+    assert out[0].tolist() == ex["expected"]
+    for h in range(H):
+        assert scores[0][h].tolist() == ex["expected_scores"][h]
+
+
+def _random_case(rng, n_pages, dup=True):
+    """Random page bytes (scale bytes 120..134, no NaN), with duplicated pages
+    to create exact ties."""
+    pool = rng.integers(0, 256, size=(n_pages, 128, 68), dtype=np.uint8)
+    pool[:, :, 64:] = rng.integers(120, 135, size=(n_pages, 128, 4))
+    if dup and n_pages >= 4:
+        pool[1] = pool[3]                      # an exact tie between pages
+    return pool.reshape(n_pages, 8704)
+
+
+def _random_q(rng, shape):
+    q = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38              # no NaN codes
+    return q
+
+
+def test_exact_bruteforce_decode():
+    rng = np.random.default_rng(1)
+    pool = _random_case(rng, 7)
+    seq_lens = np.array([3 * 128 + 5, 2, 6 * 128 + 1], dtype=np.int32)  # one padding row
+    ql, H = 3, 2
+    bt = np.array([[4, 1, 3, 0, 6, 6, 6, 6], [5, 6, 6, 6, 6, 6, 6, 6],
+                   [2, 1, 3, 0, 4, 5, 6, 6]], dtype=np.int32)
+    q = _random_q(rng, (len(seq_lens) * ql, H, 128))
+    scale = 0.375
+    out, scores, L = oracle.oracle_decode(q, pool, bt, seq_lens, ql, scale)
+    # the q_len rows of a request are its last q_len token positions
+    req = [r for r in range(len(seq_lens)) for _ in range(ql)]
+    pos = [p for s in seq_lens for p in range(int(s) - ql, int(s))]
+    ex_out, ex_sc = pins.Exact().run(q, pool, bt, req, pos, scale)
+    assert np.array_equal(out, ex_out)
+    for (row, h), s in ex_sc.items():
+        assert scores[row][h].tolist() == [float(x) for x in s]
+    pins.check_invariants(out, L)
+
+
+def test_exact_bruteforce_prefill():
+    rng = np.random.default_rng(2)
+    pool = _random_case(rng, 6)
+    ctx = np.array([250, 0], dtype=np.int32)
+    new = np.array([270, 3], dtype=np.int32)
+    cu = np.array([0, 270, 273], dtype=np.int32)
+    bt = np.array([[5, 3, 1, 0, 2, 4], [4, 0, 0, 0, 0, 0]], dtype=np.int32)
+    H = 1
+    q = _random_q(rng, (273, H, 128))
+    # exact run on a sample of rows spanning page boundaries
+    sample = np.array([0, 5, 6, 133, 134, 261, 262, 269, 270, 272])
+    out, scores, L = oracle.oracle_prefill(q, pool, bt, cu, ctx + new, ctx, 1.0)
+    # chunk rows follow the request's context tokens
+    req = np.array([0] * 270 + [1] * 3)
+    pos = np.array(list(range(250, 250 + 270)) + [0, 1, 2])
+    ex_out, ex_sc = pins.Exact().run(q[sample], pool, bt, req[sample], pos[sample], 1)
+    assert np.array_equal(out[sample], ex_out)
+    pins.check_invariants(out, L)
+
+
+def test_onehot_query_reads_single_dims():
+    """q = e_d gives s_j = max_t k_t[d], read straight from the bytes."""
+    rng = np.random.default_rng(4)
+    pool = _random_case(rng, 3, dup=False)
+    ex = pins.Exact()
+    for d in [0, 1, 31, 32, 63, 64, 100, 127]:
+        q = np.zeros((1, 1, 128), dtype=np.uint8)
+        q[0, 0, d] = 0x38
+        seq = np.array([3 * 128 + 1], dtype=np.int32)
+        bt = np.array([[2, 0, 1, 1]], dtype=np.int32)
+        _, scores, _ = oracle.oracle_decode(q, pool, bt, seq, 1)
+        for j, phys in enumerate([2, 0, 1]):
+            want = max(float(ex.token(pool[phys], t)[d]) for t in range(128))
+            assert scores[0][0][j] == want, (d, j)
+
+
+def test_zero_query_gives_ascending_ids():
+    w = W.make_workload("decode_batch_small", 0)
+    pool = W.host_pool(w, oracle.write_pages)
+    q = np.zeros_like(w.q_codes)
+    out, _, L = oracle.oracle_decode(q, pool, w.block_table, w.dec_seq_lens, w.query_len)
+    for t in range(out.shape[0]):
+        n = min(15, int(L[t]))
+        assert out[t, 0, :n].tolist() == list(range(n))
+
+
+def test_identical_pages_tie_to_lower_id():
+    rng = np.random.default_rng(9)
+    page = _random_case(rng, 1, dup=False)
+    pool = np.repeat(page, 20, axis=0)
+    q = _random_q(rng, (1, 1, 128))
+    out, _, _ = oracle.oracle_decode(q, pool, np.array([np.arange(20)[::-1]], dtype=np.int32),
+                                     np.array([20 * 128], dtype=np.int32), 1)
+    assert out[0, 0].tolist() == list(range(15)) + [19]
+
+
+def test_nan_scores_rank_last():
+    s = np.array([1.0, np.nan, 3.0, np.nan, -np.inf])
+    assert oracle.select_row(s, 5).tolist()[:5] == [2, 0, 4, 1, 3]
+
+
+def test_heap_selection_agrees():
+    rng = np.random.default_rng(12)
+    for L in [0, 1, 7, 15, 16, 40, 300]:
+        s = rng.integers(-5, 5, size=L).astype(np.float64)   # many ties
+        assert oracle.select_row(s, L).tolist() == pins.heap_select(list(s), L)
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "decode_batch_small", "multi_token_small",
+                                  "edge_short", "edge_wide", "edge_heads5"])
+def test_decode_invariants(name):
+    w = W.make_workload(name, 0)
+    pool = W.host_pool(w, oracle.write_pages)
+    out, _, L = oracle.oracle_decode(w.q_codes, pool, w.block_table, w.dec_seq_lens, w.query_len)
+    pins.check_invariants(out, L)
+    req, pos = oracle.rows_decode(w.dec_seq_lens, w.query_len)
+    assert np.array_equal(L, np.where(pos >= 0, pos // 128, -1))
+
+
+@pytest.mark.parametrize("name", ["ragged_prefill_small", "edge_prefill"])
+def test_prefill_invariants(name):
+    w = W.make_workload(name, 0)
+    pool = W.host_pool(w, oracle.write_pages)
+    out, _, L = oracle.oracle_prefill(w.q_codes, pool, w.block_table, w.cu_seqlens_q,
+                                      w.seq_lens, w.pre_ctx)
+    pins.check_invariants(out, L)
+
+
+def test_positive_scale_leaves_selection_unchanged():
+    w = W.make_workload("multi_token_small", 1)
+    pool = W.host_pool(w, oracle.write_pages)
+    base, _, _ = oracle.oracle_decode(w.q_codes, pool, w.block_table, w.dec_seq_lens, w.query_len)
+    for scale in [2.0, 0.5, 2.0 ** -20, 0.7, 3.3]:
+        o, _, _ = oracle.oracle_decode(w.q_codes, pool, w.block_table, w.dec_seq_lens,
+                                       w.query_len, scale)
+        assert np.array_equal(o, base), scale
+
+
+def test_doubling_query_codes_leaves_selection_unchanged():
+    """Adding one to the E4M3 exponent field doubles every normal q value
+    exactly; the selection must not move."""
+    w = W.make_workload("decode_batch_small", 2)
+    pool = W.host_pool(w, oracle.write_pages)
+    q = w.q_codes.copy()
+    e = (q >> 3) & 0xF
+    ok = (e >= 1) & (e <= 13)
+    q2 = q.copy()
+    q2[ok] = q[ok] + 8
+    q[~ok] = 0
+    q2[~ok] = 0
+    a, _, _ = oracle.oracle_decode(q, pool, w.block_table, w.dec_seq_lens, w.query_len)
+    b, sb, _ = oracle.oracle_decode(q2, pool, w.block_table, w.dec_seq_lens, w.query_len)
+    assert np.array_equal(a, b)
+
+
+def test_physical_placement_does_not_matter():
+    w = W.make_workload("mixed_small", 0)
+    pool = W.host_pool(w, oracle.write_pages)
+    out1, _, _ = oracle.oracle_decode(w.q_codes[:w.n_decode_rows], pool, w.block_table[:w.Rd],
+                                      w.dec_seq_lens, w.query_len)
+    perm = np.random.default_rng(99).permutation(w.num_blocks)
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    bt2 = perm[w.block_table].astype(np.int32)
+    out2, _, _ = oracle.oracle_decode(w.q_codes[:w.n_decode_rows], pool2, bt2[:w.Rd],
+                                      w.dec_seq_lens, w.query_len)
+    assert np.array_equal(out1, out2)
+
+
+def test_heads_are_independent():
+    w = W.make_workload("ragged_prefill_small", 0)
+    pool = W.host_pool(w, oracle.write_pages)
+    out, _, _ = oracle.oracle_prefill(w.q_codes, pool, w.block_table, w.cu_seqlens_q,
+                                      w.seq_lens, w.pre_ctx)
+    for h in range(w.H):
+        o1, _, _ = oracle.oracle_prefill(w.q_codes[:, h:h + 1], pool, w.block_table,
+                                         w.cu_seqlens_q, w.seq_lens, w.pre_ctx)
+        assert np.array_equal(o1[:, 0], out[:, h])
+
+
+def test_prefill_row_equals_decode_row_at_same_position():
+    w = W.make_workload("ragged_prefill_small", 3)
+    pool = W.host_pool(w, oracle.write_pages)
+    out, _, _ = oracle.oracle_prefill(w.q_codes, pool, w.block_table, w.cu_seqlens_q,
+                                      w.seq_lens, w.pre_ctx)
+    req, pos = oracle.rows_prefill(w.cu_seqlens_q, w.pre_ctx)
+    for t in [0, 17, 128, 299, 300, 555, 899]:
+        r = int(req[t])
+        d, _, _ = oracle.oracle_decode(w.q_codes[t:t + 1], pool, w.block_table[r:r + 1],
+                                       np.array([pos[t] + 1], dtype=np.int32), 1)
+        assert np.array_equal(d[0], out[t])
+        # a multi-query decode row at the same position agrees too
+        d4, _, _ = oracle.oracle_decode(np.repeat(w.q_codes[t:t + 1], 4, axis=0), pool,
+                                        w.block_table[r:r + 1],
+                                        np.array([pos[t] + 4], dtype=np.int32), 4)
+        assert np.array_equal(d4[0], out[t]) or pos[t] < 3
+
+
+def test_planted_pages_dominate():
+    w = W.make_workload("multi_token_small", 0)
+    pool = W.host_pool(w, oracle.write_pages)
+    out, _, L = oracle.oracle_decode(w.q_codes, pool, w.block_table, w.dec_seq_lens, w.query_len)
+    hits = total = 0
+    for r in range(w.Rd):
+        planted = set(w.planted_pages(r).tolist())
+        for i in range(w.query_len):
+            row = r * w.query_len + i
+            n = min(15, int(L[row]))
+            top = set(out[row, 0, :min(n, len(planted))].tolist())
+            hits += len(top & planted)
+            total += min(n, len(planted))
+    assert hits >= 0.9 * total

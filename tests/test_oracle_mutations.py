@@ -1,0 +1,190 @@
+"""Planted mistakes in the ORACLE (on the CPU): each must make at least one pin
+fail.  This shows the pins would catch a plausible error in the oracle (a
+swapped nibble, a wrong bias, an off-by-one, a wrong tie-break, sum instead
+of max, a dropped scale, a transposed operand, a wrong rounding)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import formats as F
+from oracle import indexer as I
+from tests import test_oracle_formats as TF
+from tests import test_oracle_indexer as TI
+from tests import test_oracle_plan as TP
+
+PINS = [
+    TF.test_e4m3_all_codes_match_torch_cast,
+    TF.test_e4m3_golden_points,
+    TF.test_e2m1_matches_hand_typed_table,
+    TF.test_encoder_matches_round_half_even_reference,
+    TF.test_write_then_decode_pages,
+    lambda: [TF.test_encoder_worked_examples(i) for i in range(7)],
+    TI.test_hand_worked_example,
+    TI.test_exact_bruteforce_decode,
+    TI.test_exact_bruteforce_prefill,
+    TI.test_identical_pages_tie_to_lower_id,
+    TI.test_heap_selection_agrees,
+    TI.test_nan_scores_rank_last,
+    TI.test_prefill_row_equals_decode_row_at_same_position,
+    TP.test_chunks_against_bruteforce_and_properties,
+]
+
+
+def _some_pin_fails():
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            return True
+    return False
+
+
+_orig_decode = F.decode_pages
+
+
+def _decode_pages_swapped_nibbles(page_bytes):
+    p = np.asarray(page_bytes, dtype=np.uint8).reshape(-1, 128, 68)
+    q = p.copy()
+    q[:, :, :64] = (p[:, :, :64] >> 4) | ((p[:, :, :64] & 0xF) << 4)
+    return _orig_decode(q)
+
+
+def _decode_pages_no_scale(page_bytes):
+    p = np.asarray(page_bytes, dtype=np.uint8).reshape(-1, 128, 68).copy()
+    p[:, :, 64:] = 127
+    return _orig_decode(p)
+
+
+def _decode_pages_reversed_scales(page_bytes):
+    p = np.asarray(page_bytes, dtype=np.uint8).reshape(-1, 128, 68).copy()
+    p[:, :, 64:] = p[:, :, 64:][:, :, ::-1]
+    return _orig_decode(p)
+
+
+def _decode_pages_transposed(page_bytes):
+    v = _orig_decode(page_bytes)
+    return np.swapaxes(v, 1, 2).copy()
+
+
+_orig_e4m3 = F.e4m3fn_to_float
+
+
+def _e4m3_bias8(codes):
+    return _orig_e4m3(codes) / 2.0
+
+
+_orig_select = I.select_row
+
+
+def _select_ties_high(scores, L):
+    out = np.full(16, -1, dtype=np.int32)
+    if L < 0:
+        return out
+    s = np.asarray(scores, dtype=np.float64)[:L]
+    order = sorted(range(L), key=lambda j: (-s[j] if not np.isnan(s[j]) else np.inf, -j))
+    n = min(15, L)
+    out[:n] = order[:n]
+    out[15] = L
+    return out
+
+
+def _select_nan_first(scores, L):
+    s = np.asarray(scores, dtype=np.float64).copy()
+    s[np.isnan(s)] = np.inf
+    return _orig_select(s, L)
+
+
+def _select_local_in_history(scores, L):
+    out = _orig_select(scores, L)
+    if L > 0 and L < 15:
+        out[L] = L          # local page leaks into the history slots
+    return out
+
+
+_orig_page_scores = I.page_scores
+
+
+def _page_scores_sum(q, kpages):
+    q = np.asarray(q, dtype=np.float64).reshape(-1, 128)
+    J = kpages.shape[0]
+    if J == 0:
+        return np.zeros((q.shape[0], 0))
+    return (q @ kpages.reshape(J * 128, 128).T).reshape(q.shape[0], J, 128).sum(axis=2)
+
+
+_orig_rows_decode = I.rows_decode
+
+
+def _rows_decode_shifted(seq_lens, query_len):
+    req, pos = _orig_rows_decode(seq_lens, query_len)
+    return req, pos - 1
+
+
+_orig_rows_prefill = I.rows_prefill
+
+
+def _rows_prefill_off_by_one(cu, ctx):
+    req, pos = _orig_rows_prefill(cu, ctx)
+    return req, pos + 1
+
+
+_E2M1 = F._E2M1_MAG
+
+
+def _encode_ties_away(rows, chunk=8192):
+    codes, sb = _orig_encode(rows, chunk)
+    v = np.asarray(rows, dtype=np.float64).reshape(-1, 128)
+    X = np.repeat(sb.astype(np.int64) - 127, 32, axis=1)
+    x = np.abs(v) / np.exp2(X)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    up = np.isin(x, mids)
+    mag = (codes & 7).astype(np.int64)
+    mag = np.where(up & (mag % 2 == 0) & (np.take(_E2M1, mag) < x), mag + 1, mag)
+    return (mag | (codes & 8)).astype(np.uint8), sb
+
+
+_orig_encode = F.mxfp4_encode_rows
+
+
+def _encode_exp_minus_one(rows, chunk=8192):
+    codes, sb = _orig_encode(np.asarray(rows, dtype=np.float64) * 0.5, chunk)
+    return codes, (sb.astype(np.int64) + 1).astype(np.uint8)
+
+
+_orig_chunks = oracle.prefill_chunks
+
+
+MUTATIONS = {
+    "nibbles_swapped": [(I, "decode_pages", _decode_pages_swapped_nibbles)],
+    "scale_dropped": [(I, "decode_pages", _decode_pages_no_scale)],
+    "scales_reversed": [(I, "decode_pages", _decode_pages_reversed_scales)],
+    "tokens_dims_transposed": [(I, "decode_pages", _decode_pages_transposed)],
+    "e4m3_bias_8": [(F, "e4m3fn_to_float", _e4m3_bias8), (oracle, "e4m3fn_to_float", _e4m3_bias8),
+                    (I, "e4m3fn_to_float", _e4m3_bias8)],
+    "ties_to_higher_id": [(I, "select_row", _select_ties_high), (oracle, "select_row", _select_ties_high)],
+    "nan_ranks_first": [(I, "select_row", _select_nan_first), (oracle, "select_row", _select_nan_first)],
+    "local_leaks": [(I, "select_row", _select_local_in_history)],
+    "sum_not_max": [(I, "page_scores", _page_scores_sum)],
+    "decode_positions_shifted": [(I, "rows_decode", _rows_decode_shifted),
+                                 (oracle, "rows_decode", _rows_decode_shifted)],
+    "prefill_positions_shifted": [(I, "rows_prefill", _rows_prefill_off_by_one),
+                                  (oracle, "rows_prefill", _rows_prefill_off_by_one)],
+    "encoder_ties_away": [(F, "mxfp4_encode_rows", _encode_ties_away),
+                          (oracle, "mxfp4_encode_rows", _encode_ties_away)],
+    "encoder_exponent_off_by_one": [(F, "mxfp4_encode_rows", _encode_exp_minus_one),
+                                    (oracle, "mxfp4_encode_rows", _encode_exp_minus_one)],
+    "chunks_overfill": [(oracle, "prefill_chunks",
+                         lambda s, b: _orig_chunks(s, b + 1))],
+}
+
+
+def test_pins_pass_on_the_unmodified_oracle():
+    assert not _some_pin_fails()
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    for mod, attr, fn in MUTATIONS[name]:
+        monkeypatch.setattr(mod, attr, fn)
+    assert _some_pin_fails(), f"no pin caught the planted mistake {name!r}"
