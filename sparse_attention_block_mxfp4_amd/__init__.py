@@ -1,0 +1,242 @@
+"""Python binding of ``libmi_idx.so``, the MXFP4 lightning indexer for MI355X.
+
+Argument marshalling only: every function here checks the tensors it is given
+(device, dtype, shape, contiguity), passes their device pointers and the
+current HIP stream to the C ABI declared in ``include/mi_idx.h`` (same names),
+and raises ``MiIdxError`` on a non-zero status.  All the work runs in the HIP
+kernels of ``csrc/``.  There is no fallback: importing this package fails if
+the library has not been built.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (one runtime per process, shared streams).
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmi_idx.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m sparse_attention_block_mxfp4_amd.build` "
+        "(or __graft_entry__.build()) with the ROCm toolchain")
+lib = ctypes.CDLL(LIB_PATH)
+
+_c = ctypes
+_vp, _i32, _i64, _sz, _f32 = _c.c_void_p, _c.c_int, _c.c_int64, _c.c_size_t, _c.c_float
+_SIGS = {
+    "mi_idx_version": (_c.c_char_p, []),
+    "mi_idx_last_error": (_c.c_char_p, []),
+    "mi_idx_unsupported_reason": (_c.c_char_p, [_i32, _i32, _i32, _i32, _i32, _c.c_char_p,
+                                                _i32, _i32]),
+    "mi_idx_insert_mxfp4": (_i32, [_vp, _i32, _i64, _vp, _i64, _vp, _i64, _vp]),
+    "mi_idx_decode_plan_bytes": (_sz, [_i32]),
+    "mi_idx_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "mi_idx_plan_decode": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz, _vp, _sz, _vp]),
+    "mi_idx_score_topk_decode": (_i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
+                                        _f32, _vp, _sz, _vp, _sz, _vp, _vp, _vp]),
+    "mi_idx_prefill_plan_bytes": (_sz, [_i32, _i64, _i32]),
+    "mi_idx_plan_prefill": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp, _vp, _vp]),
+    "mi_idx_score_topk_prefill": (_i32, [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
+                                         _i32, _i32, _f32, _vp, _sz, _i32, _vp, _vp, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+PAGE_TOKENS = 128
+HEAD_DIM = 128
+TOKEN_BYTES = 68
+PAGE_BYTES = 8704
+TOPK = 16
+MAX_QUERY_LEN = 8
+MAX_HEADS = 8
+
+OK, EINVAL, EUNSUPPORTED, ECAPACITY, EHIP = 0, 1, 2, 3, 4
+
+
+class MiIdxError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+def _check(status, name):
+    if status != OK:
+        raise MiIdxError(status, f"{name}: {lib.mi_idx_last_error().decode()} (status {status})")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtypes, cuda=True, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if cuda and not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_U8 = (torch.uint8,)
+_Q8 = (torch.uint8, torch.float8_e4m3fn)
+_I32 = (torch.int32,)
+
+
+def mi_idx_version():
+    return lib.mi_idx_version().decode()
+
+
+def mi_idx_unsupported_reason(topk_blocks=16, init_blocks=0, local_blocks=1, block_size=128,
+                              head_dim=128, score_type="max", num_heads=1, max_query_len=1):
+    r = lib.mi_idx_unsupported_reason(topk_blocks, init_blocks, local_blocks, block_size,
+                                      head_dim, score_type.encode(), num_heads, max_query_len)
+    return None if r is None else r.decode()
+
+
+def mi_idx_insert_mxfp4(k, slot_mapping, pages, stream=None):
+    """Quantise K rows [n, >=128] (fp32 or bf16, unit stride in the last dim)
+    to MXFP4 and write them to ``pages`` at ``slot_mapping`` [n] (int64)."""
+    _need(k, "k", (torch.float32, torch.bfloat16), contiguous=False)
+    if k.dim() != 2 or k.shape[1] < HEAD_DIM or k.stride(1) != 1:
+        raise ValueError("k must be [n, >=128] with unit stride in the last dim")
+    _need(slot_mapping, "slot_mapping", (torch.int64,))
+    _need(pages, "pages", _U8)
+    if slot_mapping.numel() != k.shape[0]:
+        raise ValueError("slot_mapping must have one slot per row of k")
+    num_blocks = pages.numel() // PAGE_BYTES
+    st = lib.mi_idx_insert_mxfp4(_ptr(k), 0 if k.dtype == torch.float32 else 1, k.stride(0),
+                                 _ptr(slot_mapping), k.shape[0], _ptr(pages), num_blocks,
+                                 _stream(stream))
+    _check(st, "mi_idx_insert_mxfp4")
+
+
+def mi_idx_decode_plan_bytes(max_reqs):
+    return int(lib.mi_idx_decode_plan_bytes(max_reqs))
+
+
+def mi_idx_decode_workspace_bytes(max_reqs, query_len, num_heads):
+    return int(lib.mi_idx_decode_workspace_bytes(max_reqs, query_len, num_heads))
+
+
+def mi_idx_plan_decode(seq_lens, query_len, max_pages, plan, workspace, stream=None):
+    _need(seq_lens, "seq_lens", _I32)
+    _need(plan, "plan", _U8)
+    _need(workspace, "workspace", _U8)
+    st = lib.mi_idx_plan_decode(_ptr(seq_lens), seq_lens.numel(), query_len, max_pages,
+                                _ptr(plan), plan.numel(), _ptr(workspace), workspace.numel(),
+                                _stream(stream))
+    _check(st, "mi_idx_plan_decode")
+
+
+def mi_idx_score_topk_decode(q, pages, block_table, seq_lens, query_len, max_pages, plan,
+                             workspace, topk_out, scale=1.0, scores_out=None, stream=None):
+    """q [R*query_len, H, 128] E4M3 (uint8 or float8_e4m3fn); topk_out
+    [R*query_len, H, 16] int32; block_table [R, >=max_pages] int32 (row stride
+    taken from the tensor)."""
+    _need(q, "q", _Q8)
+    _need(pages, "pages", _U8)
+    _need(block_table, "block_table", _I32, contiguous=False)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be 2-D with unit column stride")
+    _need(seq_lens, "seq_lens", _I32)
+    _need(topk_out, "topk_out", _I32)
+    R = seq_lens.numel()
+    H = q.shape[1] if q.dim() == 3 else 0
+    if q.dim() != 3 or q.shape[0] != R * query_len or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [{R}*{query_len}, H, 128], got {tuple(q.shape)}")
+    if tuple(topk_out.shape) != (R * query_len, H, TOPK):
+        raise ValueError(f"topk_out must be [{R * query_len}, {H}, 16]")
+    if block_table.shape[0] < R:
+        raise ValueError("block_table has fewer rows than seq_lens")
+    if scores_out is not None:
+        _need(scores_out, "scores_out", (torch.float32,))
+        if tuple(scores_out.shape) != (R * query_len, H, max_pages):
+            raise ValueError("scores_out must be [rows, H, max_pages]")
+    st = lib.mi_idx_score_topk_decode(
+        _ptr(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
+        block_table.stride(0), _ptr(seq_lens), R, query_len, H, max_pages, float(scale),
+        _ptr(plan), plan.numel(), _ptr(workspace), workspace.numel(), _ptr(topk_out),
+        _ptr(scores_out), _stream(stream))
+    _check(st, "mi_idx_score_topk_decode")
+
+
+def mi_idx_prefill_plan_bytes(num_reqs, total_q, num_heads):
+    return int(lib.mi_idx_prefill_plan_bytes(num_reqs, total_q, num_heads))
+
+
+def mi_idx_plan_prefill(cu_seqlens_q_host, seq_lens_host, num_heads, gather_budget_pages,
+                        staging, plan, stream=None):
+    """Host plan of the prefill tiles; one async copy of ``staging`` (pinned
+    host uint8 tensor) into ``plan`` (device uint8 tensor).  Returns
+    (num_tiles, num_chunks)."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_q_host, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    if cu.ndim != 1 or sl.ndim != 1 or cu.size != sl.size + 1:
+        raise ValueError("cu_seqlens_q must have one more entry than seq_lens")
+    _need(staging, "staging", _U8, cuda=False)
+    if not staging.is_pinned():
+        raise ValueError("staging must be pinned host memory")
+    _need(plan, "plan", _U8)
+    if staging.numel() < plan.numel():
+        raise ValueError("staging must be at least as large as plan")
+    tiles = ctypes.c_int(0)
+    chunks = ctypes.c_int(0)
+    st = lib.mi_idx_plan_prefill(cu.ctypes.data, sl.ctypes.data, sl.size, num_heads,
+                                 int(gather_budget_pages), _ptr(staging), _ptr(plan),
+                                 plan.numel(), ctypes.byref(chunks), ctypes.byref(tiles),
+                                 _stream(stream))
+    _check(st, "mi_idx_plan_prefill")
+    return tiles.value, chunks.value
+
+
+def mi_idx_score_topk_prefill(q, pages, block_table, cu_seqlens_q, seq_lens, context_lens,
+                              max_pages, plan, num_tiles, topk_out, scale=1.0, scores_out=None,
+                              stream=None):
+    """q [total_q, H, 128] E4M3; topk_out [total_q, H, 16] int32 (may be a
+    row slice of a larger contiguous buffer)."""
+    _need(q, "q", _Q8)
+    _need(pages, "pages", _U8)
+    _need(block_table, "block_table", _I32, contiguous=False)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be 2-D with unit column stride")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("seq_lens", seq_lens),
+                    ("context_lens", context_lens)):
+        _need(t, name, _I32)
+    _need(topk_out, "topk_out", _I32)
+    R = seq_lens.numel()
+    if cu_seqlens_q.numel() != R + 1 or context_lens.numel() != R or block_table.shape[0] < R:
+        raise ValueError("cu_seqlens_q / context_lens / block_table do not match seq_lens")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [total_q, H, 128]")
+    T, H = q.shape[0], q.shape[1]
+    if tuple(topk_out.shape) != (T, H, TOPK):
+        raise ValueError(f"topk_out must be [{T}, {H}, 16]")
+    if scores_out is not None:
+        _need(scores_out, "scores_out", (torch.float32,))
+        if tuple(scores_out.shape) != (T, H, max_pages):
+            raise ValueError("scores_out must be [total_q, H, max_pages]")
+    st = lib.mi_idx_score_topk_prefill(
+        _ptr(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
+        block_table.stride(0), _ptr(cu_seqlens_q), _ptr(seq_lens), _ptr(context_lens), R, T, H,
+        max_pages, float(scale), _ptr(plan), plan.numel(), num_tiles, _ptr(topk_out),
+        _ptr(scores_out), _stream(stream))
+    _check(st, "mi_idx_score_topk_prefill")
+
+
+__all__ = [n for n in dir() if n.startswith("mi_idx_")] + ["MiIdxError", "lib", "LIB_PATH"]

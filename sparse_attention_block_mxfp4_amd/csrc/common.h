@@ -1,0 +1,119 @@
+// Shared device helpers of the MXFP4 lightning indexer kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mi_idx.h"
+
+namespace mi_idx {
+
+constexpr int kPageTokens = MI_IDX_PAGE_TOKENS;   // tokens per page
+constexpr int kDim = MI_IDX_HEAD_DIM;             // index head dim
+constexpr int kTokenBytes = MI_IDX_TOKEN_BYTES;   // 64 code bytes + 4 scales
+constexpr int kPageBytes = MI_IDX_PAGE_BYTES;     // 8704
+constexpr int kHist = MI_IDX_HISTORY;             // ranked history slots
+constexpr int kTopk = MI_IDX_TOPK;                // + the local page
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+// 16 bytes that are only 4-byte aligned (a token's code bytes start at 68*t).
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// One 16x16x128 block-scaled MFMA: A = 16 tokens of E2M1 codes (one 32-dim
+// scale block per lane), B = 16 query columns of E4M3, fp32 result.
+//   A lane l: token (l & 15), dims [32*(l>>4), +32), 16 bytes, low nibble
+//             first; its E8M0 byte scales those 32 dims.
+//   B lane l: column (l & 15); bytes 0..15 = dims [16*(l>>4), +16) and bytes
+//             16..31 = dims [64 + 16*(l>>4), +16) (the FP8 operand order);
+//             scale byte 127 (x1).
+//   C lane l: rows 4*(l>>4) + {0..3} (tokens), column (l & 15).
+__device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4 &a, const v8i &b,
+                                            uint32_t a_scale) {
+  v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  // format codes: 4 = FP4 E2M1 (A), 0 = FP8 E4M3 (B)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, z, 4, 0, 0,
+                                                          (int)a_scale, 0, 127);
+}
+
+__device__ __forceinline__ float max4(const v4f &c) {
+  return fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w));
+}
+
+// Selection key: larger is better.  High word = the score's bits mapped to
+// an unsigned order (NaN lowest, -0 folded into +0); low word = ~id so that
+// equal scores prefer the lower id.  0 is "empty" (below every real key).
+__device__ __forceinline__ uint64_t make_key(float s, int id) {
+  uint32_t u = __float_as_uint(s);
+  uint32_t ord;
+  if (s != s) {
+    ord = 0u;
+  } else {
+    if (s == 0.0f) u = 0u;
+    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+__device__ __forceinline__ int key_id(uint64_t k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+}
+
+// Sorted (descending) list of the best kHist keys, held in registers.
+struct TopList {
+  uint64_t k[kHist];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int i = 0; i < kHist; ++i) k[i] = 0ull;
+  }
+  __device__ __forceinline__ uint64_t threshold() const { return k[kHist - 1]; }
+  // Insert x (no-op when x does not beat the current 15th key).
+  __device__ __forceinline__ void insert(uint64_t x) {
+    if (x <= k[kHist - 1]) return;
+#pragma unroll
+    for (int i = 0; i < kHist; ++i) {
+      uint64_t hi = k[i] > x ? k[i] : x;
+      uint64_t lo = k[i] > x ? x : k[i];
+      k[i] = hi;
+      x = lo;
+    }
+  }
+};
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = (uint32_t)__shfl_xor((int)lo, m, 64);
+  hi = (uint32_t)__shfl_xor((int)hi, m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Merge the lists held by lane l and lane l^m (disjoint id sets); afterwards
+// both lanes hold the best kHist of the union.
+__device__ __forceinline__ void merge_xor(TopList &t, int m) {
+  uint64_t other[kHist];
+#pragma unroll
+  for (int i = 0; i < kHist; ++i) other[i] = shfl_xor_u64(t.k[i], m);
+#pragma unroll
+  for (int i = 0; i < kHist; ++i) t.insert(other[i]);
+}
+
+// Write one (row, head) output: ranked ids, -1 padding, then the local page.
+__device__ __forceinline__ void write_row(int32_t *dst, const TopList &t,
+                                          int L) {
+  int32_t v[kTopk];
+#pragma unroll
+  for (int i = 0; i < kHist; ++i) v[i] = (L >= 0 && t.k[i] != 0ull) ? key_id(t.k[i]) : -1;
+  v[kHist] = L >= 0 ? L : -1;
+  int4 *d4 = reinterpret_cast<int4 *>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d4[i] = make_int4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
+}  // namespace mi_idx
+
+// Host-side status helpers (defined in api.hip).
+int mi_idx_fail(int status, const char *fmt, ...);
+int mi_idx_check_launch(const char *what);
+void mi_idx_clear_error();

@@ -1,0 +1,295 @@
+// Prefill: host-side tile plan + fused page scoring and top-16.
+//
+// A workgroup owns a tile of M consecutive query rows of one request and all
+// H heads: 256 query columns (column = row * H + head), 64 per wave, so each
+// wave holds four 16-column MFMA B operands in registers for the whole tile.
+// The tile walks its causal pages 0..L_max-1; each page (8704 bytes) is
+// staged once into LDS -- double-buffered, the next page's global loads in
+// flight while the current one is consumed -- and re-read by all four waves
+// as the MFMA A operand.  Rows never cross workgroups, so the top-15 of a
+// column is final when the walk ends: no merge pass.
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "common.h"
+
+namespace mi_idx {
+
+constexpr int kTileCols = 256;          // query columns per workgroup
+constexpr int kPreHeaderInts = 16;
+constexpr int kCodeStride = 80;         // LDS bytes per token of codes (64 + pad)
+constexpr int kLdsCodes = kPageTokens * kCodeStride;        // 10240
+constexpr int kLdsScales = kPageTokens * 4;                 // 512
+constexpr int kChunks = kPageBytes / 16;                    // 544 16-byte chunks
+
+inline int rows_per_tile(int H) { return kTileCols / H; }
+
+// Plan header (int32): [0] tile count, [1] rows per tile, [2] num_heads,
+// [3] chunk count.  Tile (int4): request, first row (in the request), row
+// count, page upper bound.
+
+__global__ __launch_bounds__(256) void prefill_score_kernel(
+    const uint8_t *__restrict__ q, const uint8_t *__restrict__ pages, int64_t num_blocks,
+    const int32_t *__restrict__ block_table, int64_t bt_stride,
+    const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ seq_lens,
+    const int32_t *__restrict__ context_lens, int num_reqs, int64_t total_q, int H,
+    int max_pages, float scale, const int32_t *__restrict__ plan, int32_t *__restrict__ out,
+    float *__restrict__ scores_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kLdsCodes];
+  __shared__ __attribute__((aligned(16))) uint32_t s_scales[2][kPageTokens];
+
+  if ((int)blockIdx.x >= plan[0]) return;
+  const int4 tile = reinterpret_cast<const int4 *>(plan + kPreHeaderInts)[blockIdx.x];
+  const int r = tile.x, row0 = tile.y, nrows = tile.z;
+  if (r < 0 || r >= num_reqs) return;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int t16 = lane & 15, g = lane >> 4;
+  const int ctx = context_lens[r];
+  const int sl = seq_lens[r];
+  const int64_t q0 = cu_seqlens_q[r];
+
+  // B operands: columns (wave*4 + cg)*16 + t16.
+  v8i bq[4];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {
+    const int col = (wave * 4 + cg) * 16 + t16;
+    const int rl = col / H, h = col - rl * H;
+    bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if (rl < nrows) {
+      const int64_t T = q0 + row0 + rl;
+      if (T < total_q) {
+        const uint8_t *qp = q + (T * H + h) * kDim;
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
+        bq[cg] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+  }
+  // The column this lane owns after the reduce-scatter: group g of this wave.
+  const int mycol = (wave * 4 + g) * 16 + t16;
+  const int my_rl = mycol / H, my_h = mycol - my_rl * H;
+  const int64_t myT = q0 + row0 + my_rl;
+  int myL = -1;
+  if (my_rl < nrows && myT < total_q) {
+    const int p = ctx + row0 + my_rl;
+    myL = (p >= 0 && p < sl) ? min(p >> 7, max_pages) : -1;
+  }
+  // Pages walked by the tile: every row's history is a prefix of 0..J-1.
+  int J = 0;
+  {
+    const int plast = ctx + row0 + nrows - 1;
+    J = plast >= 0 ? min(plast >> 7, max_pages) : 0;
+    J = max(J, 0);
+  }
+  TopList top;
+  top.clear();
+
+  const int32_t *bt = block_table + (int64_t)r * bt_stride;
+  uint4 pre[3];
+  auto issue = [&](int j) -> bool {
+    const int phys = bt[j];
+    if (phys < 0 || (int64_t)phys >= num_blocks) return false;
+    const uint4 *src = reinterpret_cast<const uint4 *>(pages + (int64_t)phys * kPageBytes);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int c = tid + 256 * k;
+      if (c < kChunks) pre[k] = src[c];
+    }
+    return true;
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int c = tid + 256 * k;
+      if (c < kChunks) {
+        const uint32_t w4[4] = {pre[k].x, pre[k].y, pre[k].z, pre[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int w = 4 * c + i;           // dword of the page
+          const int t = w / 17, d = w - t * 17;
+          if (d < 16)
+            *reinterpret_cast<uint32_t *>(&s_codes[buf][t * kCodeStride + 4 * d]) = w4[i];
+          else
+            s_scales[buf][t] = w4[i];
+        }
+      }
+    }
+  };
+
+  bool ok_cur = false;
+  if (J > 0) {
+    ok_cur = issue(0);
+    if (ok_cur) commit(0);
+  }
+  __syncthreads();
+  for (int j = 0; j < J; ++j) {
+    const int buf = j & 1;
+    bool ok_nxt = false;
+    if (j + 1 < J) ok_nxt = issue(j + 1);
+    if (ok_cur) {
+      float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int tl = 0; tl < 8; ++tl) {
+        const int tok = tl * 16 + t16;
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(&s_codes[buf][tok * kCodeStride + 16 * g]);
+        const uint32_t s = (s_scales[buf][tok] >> (8 * g)) & 0xFFu;
+#pragma unroll
+        for (int cg = 0; cg < 4; ++cg) m[cg] = fmaxf(m[cg], max4(mfma_fp4_fp8(a, bq[cg], s)));
+      }
+      // Reduce-scatter over the 4 lane groups: lane group g ends with the
+      // page max of its wave's column group g.
+      const bool b1 = (g >> 1) & 1, b0 = g & 1;
+      const float s0 = b1 ? m[0] : m[2], s1 = b1 ? m[1] : m[3];
+      const float k0 = fmaxf(b1 ? m[2] : m[0], __shfl_xor(s0, 32, 64));
+      const float k1 = fmaxf(b1 ? m[3] : m[1], __shfl_xor(s1, 32, 64));
+      const float sv = b0 ? k0 : k1;
+      const float v = fmaxf(b0 ? k1 : k0, __shfl_xor(sv, 16, 64));
+      if (j < myL) {
+        top.insert(make_key(v, j));
+        if (scores_out != nullptr) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
+      }
+    }
+    if (ok_nxt) commit(buf ^ 1);
+    ok_cur = ok_nxt;
+    __syncthreads();
+  }
+  if (my_rl < nrows && myT < total_q) write_row(out + (myT * H + my_h) * kTopk, top, myL);
+}
+
+}  // namespace mi_idx
+
+using namespace mi_idx;
+
+extern "C" size_t mi_idx_prefill_plan_bytes(int num_reqs, int64_t total_q, int num_heads) {
+  if (num_reqs < 0 || total_q < 0 || num_heads < 1 || num_heads > MI_IDX_MAX_HEADS) return 0;
+  const int M = rows_per_tile(num_heads);
+  const size_t tiles = (size_t)(total_q / M) + (size_t)num_reqs + 1;
+  return (size_t)kPreHeaderInts * 4 + tiles * 16;
+}
+
+extern "C" int mi_idx_plan_prefill(const int32_t *cu_seqlens_q_host, const int32_t *seq_lens_host,
+                                   int num_reqs, int num_heads, int gather_budget_pages,
+                                   void *staging_host_pinned, void *plan, size_t plan_bytes,
+                                   int *num_chunks_out_host, int *num_tiles_out_host,
+                                   void *stream) {
+  mi_idx_clear_error();
+  if (num_reqs < 0) return mi_idx_fail(MI_IDX_EINVAL, "plan_prefill: num_reqs < 0");
+  if (num_heads < 1 || num_heads > MI_IDX_MAX_HEADS)
+    return mi_idx_fail(MI_IDX_EUNSUPPORTED, "plan_prefill: num_heads %d outside 1..8", num_heads);
+  if (!staging_host_pinned || !plan || !num_tiles_out_host ||
+      (num_reqs > 0 && (!cu_seqlens_q_host || !seq_lens_host)))
+    return mi_idx_fail(MI_IDX_EINVAL, "plan_prefill: null pointer");
+  if ((uintptr_t)plan % 16) return mi_idx_fail(MI_IDX_EINVAL, "plan_prefill: plan must be 16-byte aligned");
+  if (num_reqs > 0 && cu_seqlens_q_host[0] != 0)
+    return mi_idx_fail(MI_IDX_EINVAL, "plan_prefill: cu_seqlens_q[0] must be 0");
+  for (int r = 0; r < num_reqs; ++r) {
+    const int qn = cu_seqlens_q_host[r + 1] - cu_seqlens_q_host[r];
+    if (qn < 0) return mi_idx_fail(MI_IDX_EINVAL, "plan_prefill: cu_seqlens_q decreases at %d", r);
+    if (seq_lens_host[r] < qn)
+      return mi_idx_fail(MI_IDX_EINVAL, "plan_prefill: seq_lens[%d]=%d < %d query rows", r,
+                         seq_lens_host[r], qn);
+  }
+  const int64_t total_q = num_reqs > 0 ? cu_seqlens_q_host[num_reqs] : 0;
+  const size_t need = mi_idx_prefill_plan_bytes(num_reqs, total_q, num_heads);
+  if (plan_bytes < need)
+    return mi_idx_fail(MI_IDX_ECAPACITY, "plan_prefill: plan_bytes %zu < %zu", plan_bytes, need);
+  const int M = rows_per_tile(num_heads);
+  // Greedy chunks of consecutive requests under the page budget.
+  std::vector<int> chunk_of(num_reqs, 0);
+  int nchunks = 0;
+  {
+    int first = 0;
+    while (first < num_reqs) {
+      int64_t total = std::max((seq_lens_host[first] - 1) / 128, 0);
+      int end = first + 1;
+      while (end < num_reqs) {
+        const int64_t h = std::max((seq_lens_host[end] - 1) / 128, 0);
+        if (gather_budget_pages > 0 && total + h > gather_budget_pages) break;
+        total += h;
+        ++end;
+      }
+      for (int r = first; r < end; ++r) chunk_of[r] = nchunks;
+      ++nchunks;
+      first = end;
+    }
+  }
+  struct Tile { int r, row0, nrows, pages, chunk; };
+  std::vector<Tile> tiles;
+  for (int r = 0; r < num_reqs; ++r) {
+    const int qn = cu_seqlens_q_host[r + 1] - cu_seqlens_q_host[r];
+    const int ctx_ub = seq_lens_host[r] - qn;
+    for (int row0 = 0; row0 < qn; row0 += M) {
+      const int n = std::min(M, qn - row0);
+      const int pages_ub = std::max((ctx_ub + row0 + n - 1) / 128, 0);
+      tiles.push_back({r, row0, n, pages_ub, chunk_of[r]});
+    }
+  }
+  // Chunk by chunk; inside a chunk the longest tiles first.
+  std::stable_sort(tiles.begin(), tiles.end(), [](const Tile &a, const Tile &b) {
+    if (a.chunk != b.chunk) return a.chunk < b.chunk;
+    return a.pages > b.pages;
+  });
+  int32_t *st = static_cast<int32_t *>(staging_host_pinned);
+  const size_t bytes = (size_t)kPreHeaderInts * 4 + tiles.size() * 16;
+  if (bytes > plan_bytes)
+    return mi_idx_fail(MI_IDX_ECAPACITY, "plan_prefill: %zu tiles exceed the plan", tiles.size());
+  std::fill(st, st + kPreHeaderInts, 0);
+  st[0] = (int32_t)tiles.size();
+  st[1] = M;
+  st[2] = num_heads;
+  st[3] = nchunks;
+  for (size_t i = 0; i < tiles.size(); ++i) {
+    int32_t *t = st + kPreHeaderInts + 4 * i;
+    t[0] = tiles[i].r;
+    t[1] = tiles[i].row0;
+    t[2] = tiles[i].nrows;
+    t[3] = tiles[i].pages;
+  }
+  *num_tiles_out_host = (int)tiles.size();
+  if (num_chunks_out_host) *num_chunks_out_host = nchunks;
+  hipError_t e = hipMemcpyAsync(plan, staging_host_pinned, bytes, hipMemcpyHostToDevice,
+                                (hipStream_t)stream);
+  if (e != hipSuccess)
+    return mi_idx_fail(MI_IDX_EHIP, "plan_prefill: copy failed: %s", hipGetErrorString(e));
+  return MI_IDX_OK;
+}
+
+extern "C" int mi_idx_score_topk_prefill(const uint8_t *q, const uint8_t *pages,
+                                         int64_t num_blocks, const int32_t *block_table,
+                                         int64_t bt_stride, const int32_t *cu_seqlens_q,
+                                         const int32_t *seq_lens, const int32_t *context_lens,
+                                         int num_reqs, int64_t total_q, int num_heads,
+                                         int max_pages, float scale, const void *plan,
+                                         size_t plan_bytes, int num_tiles, int32_t *topk_out,
+                                         float *scores_out, void *stream) {
+  mi_idx_clear_error();
+  if (num_heads < 1 || num_heads > MI_IDX_MAX_HEADS)
+    return mi_idx_fail(MI_IDX_EUNSUPPORTED, "score_topk_prefill: num_heads %d outside 1..8",
+                       num_heads);
+  if (num_reqs < 0 || total_q < 0 || max_pages < 0 || num_tiles < 0)
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: negative size");
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: scale must be positive and finite");
+  if (num_tiles == 0 || total_q == 0) return MI_IDX_OK;
+  if (!q || !pages || !block_table || !cu_seqlens_q || !seq_lens || !context_lens || !plan ||
+      !topk_out)
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: null pointer");
+  if (((uintptr_t)q % 16) || ((uintptr_t)pages % 16) || ((uintptr_t)topk_out % 16) ||
+      ((uintptr_t)plan % 16))
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: q, pages, topk_out and plan must be "
+                                      "16-byte aligned");
+  if (num_blocks <= 0) return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: num_blocks <= 0");
+  if (bt_stride < max_pages)
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: bt_stride < max_pages");
+  if ((size_t)kPreHeaderInts * 4 + (size_t)num_tiles * 16 > plan_bytes)
+    return mi_idx_fail(MI_IDX_ECAPACITY, "score_topk_prefill: num_tiles %d exceeds plan_bytes",
+                       num_tiles);
+  hipLaunchKernelGGL(prefill_score_kernel, dim3(num_tiles), dim3(256), 0, (hipStream_t)stream, q,
+                     pages, num_blocks, block_table, bt_stride, cu_seqlens_q, seq_lens,
+                     context_lens, num_reqs, total_q, num_heads, max_pages, scale,
+                     (const int32_t *)plan, topk_out, scores_out);
+  return mi_idx_check_launch("score_topk_prefill");
+}
