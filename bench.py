@@ -39,7 +39,22 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--pool-copies", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy three times (the reference "
+                        "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return p.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
 def algorithmic(w):
@@ -134,6 +149,9 @@ def main():
               "(the multi-GPU sharding is described in DESIGN.md, not implemented).",
               file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     import sparse_attention_block_mxfp4_amd as m

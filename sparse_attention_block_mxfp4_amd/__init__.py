@@ -35,7 +35,7 @@ _SIGS = {
     "mi_idx_insert_mxfp4": (_i32, [_vp, _i32, _i64, _vp, _i64, _vp, _i64, _vp]),
     "mi_idx_decode_plan_bytes": (_sz, [_i32]),
     "mi_idx_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
-    "mi_idx_plan_decode": (_i32, [_vp, _i32, _i32, _i32, _vp, _sz, _vp, _sz, _vp]),
+    "mi_idx_plan_decode": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _sz, _vp]),
     "mi_idx_score_topk_decode": (_i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
                                         _f32, _vp, _sz, _vp, _sz, _vp, _vp, _vp]),
     "mi_idx_prefill_plan_bytes": (_sz, [_i32, _i64, _i32]),
@@ -134,13 +134,14 @@ def mi_idx_decode_workspace_bytes(max_reqs, query_len, num_heads):
     return int(lib.mi_idx_decode_workspace_bytes(max_reqs, query_len, num_heads))
 
 
-def mi_idx_plan_decode(seq_lens, query_len, max_pages, plan, workspace, stream=None):
+def mi_idx_plan_decode(seq_lens, query_len, num_heads, max_pages, plan, workspace,
+                       stream=None):
     _need(seq_lens, "seq_lens", _I32)
     _need(plan, "plan", _U8)
     _need(workspace, "workspace", _U8)
-    st = lib.mi_idx_plan_decode(_ptr(seq_lens), seq_lens.numel(), query_len, max_pages,
-                                _ptr(plan), plan.numel(), _ptr(workspace), workspace.numel(),
-                                _stream(stream))
+    st = lib.mi_idx_plan_decode(_ptr(seq_lens), seq_lens.numel(), query_len, num_heads,
+                                max_pages, _ptr(plan), plan.numel(), _ptr(workspace),
+                                workspace.numel(), _stream(stream))
     _check(st, "mi_idx_plan_decode")
 
 

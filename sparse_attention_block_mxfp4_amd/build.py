@@ -27,6 +27,9 @@ def build(verbose=False, extra=()):
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           # device code: no NaN operands reach max/compare (keys test NaN on
+           # the bits), MFMA results stay in VGPRs
+           "-Xarch_device", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", os.path.join(ROOT, "include"), *extra, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)

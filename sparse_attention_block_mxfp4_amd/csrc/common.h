@@ -48,7 +48,7 @@ __device__ __forceinline__ float max4(const v4f &c) {
 __device__ __forceinline__ uint64_t make_key(float s, int id) {
   uint32_t u = __float_as_uint(s);
   uint32_t ord;
-  if (s != s) {
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) {   // NaN (tested on the bits)
     ord = 0u;
   } else {
     if (s == 0.0f) u = 0u;
@@ -97,6 +97,14 @@ __device__ __forceinline__ void merge_xor(TopList &t, int m) {
   for (int i = 0; i < kHist; ++i) other[i] = shfl_xor_u64(t.k[i], m);
 #pragma unroll
   for (int i = 0; i < kHist; ++i) t.insert(other[i]);
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Write one (row, head) output: ranked ids, -1 padding, then the local page.

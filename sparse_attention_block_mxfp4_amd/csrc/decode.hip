@@ -1,133 +1,152 @@
-// Decode: device-side work-map plan + fused page scoring and top-16.
+// Decode: device-side work-map plan, fused page scoring with a per-wave
+// top-15, and a per-request merge into the [T, H, 16] output.
 //
 // Plan (one workgroup): history pages of request r are 0..hist_r-1 with
 // hist_r = (seq_len_r - 1) / 128 (the last query's local page bounds every
 // row of the request), clamped to max_pages.  A chunk size is picked so that
 // the whole batch splits into about kTargetItems equal work items (at least
-// kMinChunk pages each); every request gets max(1, ceil(hist_r / chunk))
-// items.  Items = (request, first page, end page, first item of the request,
-// item count of the request).
+// kMinChunk pages each); every request gets max(1, ceil(hist_r / chunk_r))
+// items, each one wave's worth of work, with chunk_r = chunk raised where
+// needed so that no request has more than kMaxItemsPerReq items.  Items = (request, first page, end
+// page); the request's first item and item count go to the workspace.
 //
-// Score (one wave per work item): stream the item's pages through the MFMA
-// with the request's query rows as the B operand, reduce each page to its max
-// over tokens, keep a running top-15 per query column in registers, write the
-// list to the workspace, and the LAST item of a request to arrive (an atomic
-// counter per request) merges the request's lists and writes the output rows.
+// Score (4 independent waves per workgroup, one item each): a wave streams
+// its pages through the MFMA with the request's query rows as the B operand,
+// reduces each page to its max over tokens, keeps a running top-15 per query
+// column in registers and writes the lists to the workspace.
+//
+// Merge (one workgroup per request, a second launch on the same stream, so
+// the lists written by every XCD are visible without device-wide fences):
+// merges the request's item lists into the 16 output slots of every row.
 #include <cmath>
 
 #include "common.h"
 
 namespace mi_idx {
 
-constexpr int kTargetItems = 2048;
+constexpr int kTargetItems = 2048;    // ~8 waves per CU
 constexpr int kMinChunk = 4;
 constexpr int kPlanHeaderInts = 16;
-constexpr int kItemInts = 8;
+constexpr int kItemInts = 4;
 constexpr size_t kWsHeaderBytes = 256;
+constexpr int kListKeys = 16;         // 15 keys + an empty slot: 128-byte lists
+constexpr int kDepth = 3;             // pages in flight per wave (register ring)
+constexpr int kMergeKeys = 2048;      // LDS keys for the bounds of one merge pass
+constexpr int kCandKeys = 2048;       // LDS candidate keys of one merge pass
+constexpr int kMaxItemsPerReq = 256;  // bounds the merge's O(n^2) ranking
 
 // Plan header (int32): [0] item count, [1] chunk pages, [2] num_reqs,
-// [3] query_len, [4] max_pages, [5] capacity.
-struct DecodeItem {
-  int r, j0, j1, first, count, pad0, pad1, pad2;
-};
+// [3] query_len, [4] max_pages, [5] capacity.  Items follow (int4 each).
+// Workspace: [0, 256) header (word 0: error bits), then the item lists
+// [capacity][rows][kListKeys] uint64, then (first item, item count) int2 per
+// request.
 
 __host__ __device__ inline size_t decode_capacity(int max_reqs) {
   return (size_t)max_reqs + kTargetItems;
 }
 
+__host__ __device__ inline size_t lists_bytes(size_t capacity, int rows) {
+  return capacity * (size_t)rows * kListKeys * 8;
+}
+
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *__restrict__ seq_lens,
                                                            int num_reqs, int max_pages,
-                                                           int query_len, int capacity,
+                                                           int query_len, int capacity, int rows,
                                                            int32_t *__restrict__ plan,
-                                                           uint32_t *__restrict__ ws_words) {
+                                                           uint8_t *__restrict__ ws) {
   __shared__ long long s_part[1024];
   __shared__ int s_chunk;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
+  int2 *req_info = reinterpret_cast<int2 *>(ws + kWsHeaderBytes + lists_bytes(capacity, rows));
   // Contiguous segment of requests per thread.
   const int per = (num_reqs + nt - 1) / nt;
   const int r0 = min(num_reqs, tid * per), r1 = min(num_reqs, r0 + per);
   long long hsum = 0;
   for (int r = r0; r < r1; ++r) {
-    int sl = seq_lens[r];
-    int h = sl >= 1 ? (sl - 1) >> 7 : 0;
-    hsum += min(h, max_pages);
+    const int sl = seq_lens[r];
+    hsum += min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
   }
   s_part[tid] = hsum;
   __syncthreads();
   if (tid == 0) {
     long long total = 0;
     for (int i = 0; i < nt; ++i) total += s_part[i];
-    long long c = (total + kTargetItems - 1) / kTargetItems;
+    const long long c = (total + kTargetItems - 1) / kTargetItems;
     s_chunk = (int)max((long long)kMinChunk, c);
   }
   __syncthreads();
   const int chunk = s_chunk;
+  auto chunk_of = [&](int h) {
+    return max(chunk, (h + kMaxItemsPerReq - 1) / kMaxItemsPerReq);
+  };
   // Item counts and their exclusive scan over the thread segments.
   long long cnt = 0;
   for (int r = r0; r < r1; ++r) {
-    int sl = seq_lens[r];
-    int h = min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
-    cnt += max(1, (h + chunk - 1) / chunk);
+    const int sl = seq_lens[r];
+    const int h = min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
+    const int c = chunk_of(h);
+    cnt += max(1, (h + c - 1) / c);
   }
   __syncthreads();
   s_part[tid] = cnt;
   __syncthreads();
   // Hillis-Steele inclusive scan over the 1024 partial counts.
   for (int off = 1; off < nt; off <<= 1) {
-    long long v = tid >= off ? s_part[tid - off] : 0;
+    const long long v = tid >= off ? s_part[tid - off] : 0;
     __syncthreads();
     s_part[tid] += v;
     __syncthreads();
   }
   long long first = s_part[tid] - cnt;
   for (int r = r0; r < r1; ++r) {
-    int sl = seq_lens[r];
-    int h = min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
-    int n = max(1, (h + chunk - 1) / chunk);
+    const int sl = seq_lens[r];
+    const int h = min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
+    const int c = chunk_of(h);
+    const int n = max(1, (h + c - 1) / c);
     for (int i = 0; i < n; ++i) {
-      long long it = first + i;
-      if (it < capacity) {
-        int4 *dst = reinterpret_cast<int4 *>(plan + kPlanHeaderInts + it * kItemInts);
-        dst[0] = make_int4(r, min(h, i * chunk), min(h, (i + 1) * chunk), (int)first);
-        dst[1] = make_int4(n, 0, 0, 0);
-      }
+      const long long it = first + i;
+      if (it < capacity)
+        reinterpret_cast<int4 *>(plan + kPlanHeaderInts)[it] =
+            make_int4(r, min(h, i * c), min(h, (i + 1) * c), 0);
     }
+    req_info[r] = make_int2((int)first, n);
     first += n;
-    ws_words[kWsHeaderBytes / 4 + r] = 0u;   // arrival counter of request r
   }
   if (tid == nt - 1) {
-    long long total_items = s_part[nt - 1];
+    const long long total_items = s_part[nt - 1];
     plan[0] = (int)min(total_items, (long long)capacity);
     plan[1] = chunk;
     plan[2] = num_reqs;
     plan[3] = query_len;
     plan[4] = max_pages;
     plan[5] = capacity;
-    ws_words[0] = total_items > capacity ? 2u : 0u;   // error word
+    reinterpret_cast<uint32_t *>(ws)[0] = total_items > capacity ? 2u : 0u;   // error bits
   }
 }
 
-template <int NCG>
-__global__ __launch_bounds__(64) void decode_score_kernel(
+__device__ __forceinline__ uint64_t *item_list(uint64_t *lists, int item, int rows, int col) {
+  return lists + ((size_t)item * rows + col) * kListKeys;
+}
+
+template <int NCG, bool kScores>
+__global__ __launch_bounds__(256) void decode_score_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ pages, int64_t num_blocks,
     const int32_t *__restrict__ block_table, int64_t bt_stride,
     const int32_t *__restrict__ seq_lens, int num_reqs, int query_len, int H, int max_pages,
     float scale, const int32_t *__restrict__ plan, uint8_t *__restrict__ ws,
-    int32_t *__restrict__ out, float *__restrict__ scores_out) {
-  const int item = blockIdx.x;
+    float *__restrict__ scores_out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int item = blockIdx.x * 4 + (tid >> 6);
   if (item >= plan[0]) return;
-  const DecodeItem it = *reinterpret_cast<const DecodeItem *>(plan + kPlanHeaderInts +
-                                                                (size_t)item * kItemInts);
-  const int lane = threadIdx.x;
-  const int t16 = lane & 15, g = lane >> 4;
-  const int r = it.r;
+  const int4 it = reinterpret_cast<const int4 *>(plan + kPlanHeaderInts)[item];
+  const int r = it.x, j0 = it.y, j1 = it.z;
   if (r < 0 || r >= num_reqs) return;
+  const int t16 = lane & 15, g = lane >> 4;
   const int rows = query_len * H;
   const int sl = seq_lens[r];
-  uint32_t *ws_words = reinterpret_cast<uint32_t *>(ws);
-  uint64_t *partial = reinterpret_cast<uint64_t *>(
-      ws + kWsHeaderBytes + (((size_t)4 * num_reqs + 255) & ~(size_t)255));
+  uint64_t *lists = reinterpret_cast<uint64_t *>(ws + kWsHeaderBytes);
 
   // Query fragments (B operand) and the causal bound of each column.
   v8i bq[NCG];
@@ -153,130 +172,258 @@ __global__ __launch_bounds__(64) void decode_score_kernel(
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) top[cg].clear();
 
+  // The item's pages are walked in segments of 64: one vector load brings
+  // the segment's block-table entries (one per lane) and readlane hands
+  // them out.  Inside a segment a ring of kDepth pages lives in registers:
+  // kDepth-1 pages are in flight while one goes through the MFMA.  Ring
+  // indices are compile-time (the ring loop is unrolled), so there are no
+  // register copies, and every page load is unconditional -- a position past
+  // the segment re-loads its last page (a cache hit) and an invalid page id
+  // loads page 0 and is skipped -- so the wait counts stay exact.
   const int32_t *bt = block_table + (int64_t)r * bt_stride;
   bool bad = false;
-  // Page pipeline: the next page's 8 tiles are in flight while the current
-  // page goes through the MFMA.  Block-table entries are fetched 64 at a time
-  // (one per lane) and broadcast with readlane.
-  u32x4 a_cur[8], a_nxt[8];
-  uint32_t s_cur[8], s_nxt[8];
-  int bt_base = it.j0;
-  int bt_lane = (bt_base + lane < it.j1) ? bt[bt_base + lane] : -1;
-  auto phys_of = [&](int j) -> int {
-    if (j - bt_base >= 64) {
-      bt_base += 64;
-      bt_lane = (bt_base + lane < it.j1) ? bt[bt_base + lane] : -1;
-    }
-    return __builtin_amdgcn_readlane(bt_lane, j - bt_base);
-  };
-  auto issue = [&](int phys, u32x4 *a, uint32_t *sc) {
-    const uint8_t *page = pages + (int64_t)phys * kPageBytes;
-#pragma unroll
-    for (int tile = 0; tile < 8; ++tile) {
-      const uint8_t *tp = page + (tile * 16 + t16) * kTokenBytes;
-      const u32x4a4 a4 = *reinterpret_cast<const u32x4a4 *>(tp + 16 * g);
-      a[tile] = u32x4{a4.x, a4.y, a4.z, a4.w};
-      sc[tile] = tp[64 + g];
-    }
-  };
-  int phys_cur = it.j0 < it.j1 ? phys_of(it.j0) : -1;
-  bool ok_cur = phys_cur >= 0 && (int64_t)phys_cur < num_blocks;
-  if (ok_cur) issue(phys_cur, a_cur, s_cur);
-  for (int j = it.j0; j < it.j1; ++j) {
-    bool ok_nxt = false;
-    if (j + 1 < it.j1) {
-      const int phys_nxt = phys_of(j + 1);
-      ok_nxt = phys_nxt >= 0 && (int64_t)phys_nxt < num_blocks;
-      if (ok_nxt) issue(phys_nxt, a_nxt, s_nxt);
-    }
-    if (ok_cur) {
-      float m[NCG];
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) m[cg] = -INFINITY;
+  u32x4 a[kDepth][8];
+  uint32_t s[kDepth][8];
+  bool okb[kDepth];
+  for (int seg = j0; seg < j1; seg += 64) {
+    const int ns = min(64, j1 - seg);
+    const int bt_lane = lane < ns ? bt[seg + lane] : -1;
+    auto issue = [&](int i, u32x4 *ab, uint32_t *sb) -> bool {
+      const int phys = __builtin_amdgcn_readlane(bt_lane, min(i, ns - 1));
+      const bool valid = phys >= 0 && (int64_t)phys < num_blocks;
+      const uint8_t *page = pages + (int64_t)(valid ? phys : 0) * kPageBytes;
 #pragma unroll
       for (int tile = 0; tile < 8; ++tile) {
-#pragma unroll
-        for (int cg = 0; cg < NCG; ++cg)
-          m[cg] = fmaxf(m[cg], max4(mfma_fp4_fp8(a_cur[tile], bq[cg], s_cur[tile])));
+        const uint8_t *tp = page + (tile * 16 + t16) * kTokenBytes;
+        const u32x4a4 a4 = *reinterpret_cast<const u32x4a4 *>(tp + 16 * g);
+        ab[tile] = u32x4{a4.x, a4.y, a4.z, a4.w};
+        sb[tile] = tp[64 + g];
       }
+      if (i < ns && !valid) bad = true;
+      return i < ns && valid;
+    };
+    // Keep the prologue's pages in ring order (no interleaving), as in the
+    // steady state, so the wait counts at the loop head stay exact.
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-        float v = m[cg];
-        v = fmaxf(v, __shfl_xor(v, 16, 64));
-        v = fmaxf(v, __shfl_xor(v, 32, 64));
-        if (j < Lc[cg]) {
-          top[cg].insert(make_key(v, j));
-          if (scores_out != nullptr && g == 0) {
-            const int col = cg * 16 + t16;
-            const int i = col / H, h = col - (col / H) * H;
-            const int64_t T = (int64_t)r * query_len + i;
-            scores_out[(T * H + h) * max_pages + j] = v * scale;
+    for (int d = 0; d < kDepth - 1; ++d) {
+      okb[d] = issue(d, a[d], s[d]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int ib = 0; ib < ns; ib += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int i = ib + u;
+        const int j = seg + i;
+        const int un = (u + kDepth - 1) % kDepth;
+        okb[un] = issue(i + kDepth - 1, a[un], s[un]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (okb[u]) {
+          float m[NCG];
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) m[cg] = -INFINITY;
+#pragma unroll
+          for (int tile = 0; tile < 8; ++tile) {
+#pragma unroll
+            for (int cg = 0; cg < NCG; ++cg)
+              m[cg] = fmaxf(m[cg], max4(mfma_fp4_fp8(a[u][tile], bq[cg], s[u][tile])));
+          }
+#pragma unroll
+          for (int cg = 0; cg < NCG; ++cg) {
+            float v = m[cg];
+            v = fmaxf(v, __shfl_xor(v, 16, 64));
+            v = fmaxf(v, __shfl_xor(v, 32, 64));
+            if (j < Lc[cg]) {
+              top[cg].insert(make_key(v, j));
+              if (kScores && g == 0) {
+                const int col = cg * 16 + t16;
+                const int qi = col / H, h = col - (col / H) * H;
+                const int64_t T = (int64_t)r * query_len + qi;
+                scores_out[(T * H + h) * max_pages + j] = v * scale;
+              }
+            }
           }
         }
       }
-    } else {
-      bad = true;
     }
-#pragma unroll
-    for (int tile = 0; tile < 8; ++tile) {
-      a_cur[tile] = a_nxt[tile];
-      s_cur[tile] = s_nxt[tile];
-    }
-    ok_cur = ok_nxt;
   }
-  if (bad && lane == 0) atomicOr(&ws_words[0], 1u);
+  if (bad && lane == 0) atomicOr(reinterpret_cast<uint32_t *>(ws), 1u);
 
-  // Publish this item's lists.
+  // This item's lists (16 keys each, the last one empty).
   if (g == 0) {
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const int col = cg * 16 + t16;
       if (col < rows) {
-        uint64_t *dst = partial + ((size_t)item * rows + col) * kHist;
+        u32x4 *dst = reinterpret_cast<u32x4 *>(item_list(lists, item, rows, col));
 #pragma unroll
-        for (int k = 0; k < kHist; ++k) dst[k] = top[cg].k[k];
-      }
-    }
-  }
-  __threadfence();
-  uint32_t old = 0;
-  if (lane == 0) old = atomicAdd(&ws_words[kWsHeaderBytes / 4 + r], 1u);
-  old = (uint32_t)__shfl((int)old, 0, 64);
-  if (old + 1 != (uint32_t)it.count) return;
-  __threadfence();
-
-  // Last arrival: merge the request's lists, 4 lane groups over the items.
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const int col = cg * 16 + t16;
-    TopList acc;
-    acc.clear();
-    if (col < rows) {
-      for (int x = it.first + g; x < it.first + it.count; x += 4) {
-        const uint64_t *src = partial + ((size_t)x * rows + col) * kHist;
-        for (int k = 0; k < kHist; ++k) {
-          const uint64_t key = __builtin_nontemporal_load(src + k);
-          if (key <= acc.threshold()) break;
-          acc.insert(key);
+        for (int k2 = 0; k2 < kListKeys / 2; ++k2) {
+          const uint64_t x0 = top[cg].k[2 * k2];
+          const uint64_t x1 = 2 * k2 + 1 < kHist ? top[cg].k[2 * k2 + 1] : 0ull;
+          dst[k2] = u32x4{(uint32_t)x0, (uint32_t)(x0 >> 32), (uint32_t)x1, (uint32_t)(x1 >> 32)};
         }
       }
     }
-    merge_xor(acc, 16);
-    merge_xor(acc, 32);
-    if (g == 0 && col < rows) {
-      const int i = col / H, h = col - (col / H) * H;
-      const int64_t T = (int64_t)r * query_len + i;
-      write_row(out + (T * H + h) * kTopk, acc, Lc[cg]);
-    }
   }
-  if (lane == 0) ws_words[kWsHeaderBytes / 4 + r] = 0u;   // ready for the next call
+}
+
+struct MergeSmem {
+  uint64_t t[kMergeKeys];     // the lists' top keys
+  uint64_t cand[kCandKeys];   // keys at or above a column's bound
+  uint64_t thr[64];
+  uint32_t ncand[64];
+  uint32_t over[64];
+};
+
+// One workgroup per request: merge the request's n item lists, for every
+// column (row x head), into its 16 output slots.
+//
+// Any 15 distinct keys bound the 15th best key of the union from below; the
+// 15th largest of the lists' top-K keys (K = ceil(15 / n), so 1 once there
+// are 15 lists or more) is such a bound, and every key of the final top-15
+// is at or above it.  The keys at or above the bound are gathered and ranked by
+// counting (keys are distinct).  Columns go in batches that fit the LDS
+// arrays; a column whose candidates overflow its share is merged by
+// per-lane insertion and a butterfly instead (slower, same result).
+__global__ __launch_bounds__(256) void decode_merge_kernel(
+    const int32_t *__restrict__ seq_lens, int num_reqs, int query_len, int H, int max_pages,
+    const int32_t *__restrict__ plan, const uint8_t *__restrict__ ws,
+    int32_t *__restrict__ out) {
+  __shared__ MergeSmem sm;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int rows = query_len * H;
+  const int capacity = plan[5];
+  const uint64_t *lists = reinterpret_cast<const uint64_t *>(ws + kWsHeaderBytes);
+  const int2 info = reinterpret_cast<const int2 *>(ws + kWsHeaderBytes +
+                                                   lists_bytes(capacity, rows))[r];
+  const int first = info.x, n = info.y;
+  const int sl = seq_lens[r];
+  auto key = [&](int c, int x, int k) -> uint64_t {
+    return lists[((size_t)(first + x) * rows + c) * kListKeys + k];
+  };
+  auto emit = [&](int c, int slot, uint64_t v) {
+    const int qi = c / H, h = c - (c / H) * H;
+    const int64_t T = (int64_t)r * query_len + qi;
+    const int p = sl - query_len + qi;
+    const int L = p >= 0 ? min(p >> 7, max_pages) : -1;
+    out[(T * H + h) * kTopk + slot] = (L >= 0 && v != 0ull) ? key_id(v) : -1;
+  };
+  const int K = n >= kHist ? 1 : (kHist + n - 1) / max(n, 1);
+  const int per_col = max(n * K, 1);
+  const int batch = max(1, min(rows, min(kMergeKeys / per_col, 64)));
+  for (int c0 = 0; c0 < rows; c0 += batch) {
+    const int nc = min(batch, rows - c0);
+    const int cand_cap = kCandKeys / nc;
+    // 1. every list's top-K keys
+    for (int p = tid; p < nc * per_col; p += nt) {
+      const int cl = p / per_col, i = p - cl * per_col;
+      const int x = i / K, k = i - x * K;
+      sm.t[p] = n > 0 ? key(c0 + cl, x, k) : 0ull;
+    }
+    for (int c = tid; c < nc; c += nt) {
+      sm.thr[c] = 0ull;
+      sm.ncand[c] = 0u;
+      sm.over[c] = 0u;
+    }
+    __syncthreads();
+    // 2. the bound: the 15th largest of those keys (none if fewer than 15)
+    for (int p = tid; p < nc * per_col; p += nt) {
+      const int cl = p / per_col;
+      const uint64_t me = sm.t[p];
+      if (me == 0ull) continue;
+      const uint64_t *row = sm.t + cl * per_col;
+      int rank = 0;
+      for (int i = 0; i < per_col; ++i) rank += row[i] > me ? 1 : 0;
+      if (rank == kHist - 1) sm.thr[cl] = me;
+    }
+    __syncthreads();
+    // 3. gather every key at or above the bound: the top-K keys from LDS,
+    // deeper keys from the list only when its K-th key reaches the bound
+    for (int p = tid; p < nc * n; p += nt) {
+      const int cl = p / n, x = p - cl * n;
+      const uint64_t thr = sm.thr[cl] ? sm.thr[cl] : 1ull;
+      const uint64_t *tk = sm.t + cl * per_col + x * K;
+      int k = 0;
+      for (; k < K; ++k) {
+        const uint64_t v = tk[k];
+        if (v < thr) break;
+        const uint32_t pos = atomicAdd(&sm.ncand[cl], 1u);
+        if (pos < (uint32_t)cand_cap) sm.cand[cl * cand_cap + pos] = v;
+        else sm.over[cl] = 1u;
+      }
+      // deeper keys, two per 16-byte load, while they reach the bound
+      bool more = k == K;
+      for (int k2 = K & ~1; more && k2 < kListKeys; k2 += 2) {
+        const u32x4 v4 = *reinterpret_cast<const u32x4 *>(
+            lists + ((size_t)(first + x) * rows + c0 + cl) * kListKeys + k2);
+        const uint64_t pair[2] = {((uint64_t)v4.y << 32) | v4.x, ((uint64_t)v4.w << 32) | v4.z};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          if (k2 + e < k || !more) continue;
+          const uint64_t v = pair[e];
+          if (k2 + e >= kHist || v < thr) {
+            more = false;
+            continue;
+          }
+          const uint32_t pos = atomicAdd(&sm.ncand[cl], 1u);
+          if (pos < (uint32_t)cand_cap) sm.cand[cl * cand_cap + pos] = v;
+          else sm.over[cl] = 1u;
+        }
+      }
+    }
+    __syncthreads();
+    // 4. rank them; slots past the candidates are empty
+    for (int p = tid; p < nc * kHist; p += nt) {
+      const int cl = p / kHist, k = p - cl * kHist;
+      if (!sm.over[cl] && k >= (int)sm.ncand[cl]) emit(c0 + cl, k, 0ull);
+    }
+    for (int p = tid; p < nc * cand_cap; p += nt) {
+      const int cl = p / cand_cap, i = p - cl * cand_cap;
+      const int m = (int)sm.ncand[cl];
+      if (sm.over[cl] || i >= m) continue;
+      const uint64_t *cc = sm.cand + cl * cand_cap;
+      const uint64_t me = cc[i];
+      int rank = 0;
+      for (int b = 0; b < m; ++b) rank += cc[b] > me ? 1 : 0;
+      if (rank < kHist) emit(c0 + cl, rank, me);
+    }
+    // Overflowed columns: one wave, per-lane insertion, then a butterfly.
+    if (tid < 64) {
+      for (int cl = 0; cl < nc; ++cl) {
+        if (!sm.over[cl]) continue;
+        TopList acc;
+        acc.clear();
+        for (int x = tid; x < n; x += 64) {
+          for (int k = 0; k < kHist; ++k) {
+            const uint64_t v = key(c0 + cl, x, k);
+            if (v <= acc.threshold()) break;
+            acc.insert(v);
+          }
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) merge_xor(acc, m);
+        if (tid < kHist) {
+          uint64_t v = 0ull;
+#pragma unroll
+          for (int k = 0; k < kHist; ++k) v = (k == tid) ? acc.k[k] : v;
+          emit(c0 + cl, tid, v);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // Slot 15: the local page (-1 for a padding row).
+  for (int c = tid; c < rows; c += nt) {
+    const int qi = c / H, h = c - (c / H) * H;
+    const int64_t T = (int64_t)r * query_len + qi;
+    const int p = sl - query_len + qi;
+    out[(T * H + h) * kTopk + kHist] = p >= 0 ? min(p >> 7, max_pages) : -1;
+  }
 }
 
 }  // namespace mi_idx
 
 using namespace mi_idx;
-
-static size_t ws_counters_bytes(int max_reqs) { return ((size_t)4 * max_reqs + 255) & ~(size_t)255; }
 
 extern "C" size_t mi_idx_decode_plan_bytes(int max_reqs) {
   if (max_reqs < 0) return 0;
@@ -285,41 +432,41 @@ extern "C" size_t mi_idx_decode_plan_bytes(int max_reqs) {
 
 extern "C" size_t mi_idx_decode_workspace_bytes(int max_reqs, int query_len, int num_heads) {
   if (max_reqs < 0 || query_len < 1 || num_heads < 1) return 0;
-  return kWsHeaderBytes + ws_counters_bytes(max_reqs) +
-         decode_capacity(max_reqs) * (size_t)query_len * num_heads * kHist * 8;
+  return kWsHeaderBytes + lists_bytes(decode_capacity(max_reqs), query_len * num_heads) +
+         (size_t)8 * max_reqs;
 }
 
 static int plan_capacity(size_t plan_bytes) {
   if (plan_bytes < (size_t)kPlanHeaderInts * 4) return 0;
-  size_t c = (plan_bytes - kPlanHeaderInts * 4) / (kItemInts * 4);
+  const size_t c = (plan_bytes - kPlanHeaderInts * 4) / (kItemInts * 4);
   return c > 0x7FFFFFF ? 0x7FFFFFF : (int)c;
 }
 
 static int check_decode_sizes(const char *who, int num_reqs, int query_len, int num_heads,
-                              int max_pages, size_t plan_bytes, size_t ws_bytes, bool need_heads) {
+                              int max_pages, size_t plan_bytes, size_t ws_bytes) {
   if (num_reqs < 0) return mi_idx_fail(MI_IDX_EINVAL, "%s: num_reqs %d < 0", who, num_reqs);
   if (query_len < 1 || query_len > MI_IDX_MAX_QUERY_LEN)
     return mi_idx_fail(MI_IDX_EUNSUPPORTED, "%s: query_len %d outside 1..8", who, query_len);
-  if (need_heads && (num_heads < 1 || num_heads > MI_IDX_MAX_HEADS))
+  if (num_heads < 1 || num_heads > MI_IDX_MAX_HEADS)
     return mi_idx_fail(MI_IDX_EUNSUPPORTED, "%s: num_heads %d outside 1..8", who, num_heads);
   if (max_pages < 0) return mi_idx_fail(MI_IDX_EINVAL, "%s: max_pages %d < 0", who, max_pages);
   const int cap = plan_capacity(plan_bytes);
   if ((size_t)cap < decode_capacity(num_reqs))
     return mi_idx_fail(MI_IDX_ECAPACITY, "%s: plan_bytes %zu < %zu needed for %d requests", who,
                        plan_bytes, mi_idx_decode_plan_bytes(num_reqs), num_reqs);
-  size_t need = kWsHeaderBytes + ws_counters_bytes(num_reqs);
-  if (need_heads) need += (size_t)cap * query_len * num_heads * kHist * 8;
+  const size_t need =
+      kWsHeaderBytes + lists_bytes(cap, query_len * num_heads) + (size_t)8 * num_reqs;
   if (ws_bytes < need)
     return mi_idx_fail(MI_IDX_ECAPACITY, "%s: ws_bytes %zu < %zu needed", who, ws_bytes, need);
   return MI_IDX_OK;
 }
 
 extern "C" int mi_idx_plan_decode(const int32_t *seq_lens, int num_reqs, int query_len,
-                                  int max_pages, void *plan, size_t plan_bytes, void *workspace,
-                                  size_t ws_bytes, void *stream) {
+                                  int num_heads, int max_pages, void *plan, size_t plan_bytes,
+                                  void *workspace, size_t ws_bytes, void *stream) {
   mi_idx_clear_error();
-  int st = check_decode_sizes("plan_decode", num_reqs, query_len, 1, max_pages, plan_bytes,
-                              ws_bytes, false);
+  int st = check_decode_sizes("plan_decode", num_reqs, query_len, num_heads, max_pages,
+                              plan_bytes, ws_bytes);
   if (st) return st;
   if (!plan || !workspace || (num_reqs > 0 && !seq_lens))
     return mi_idx_fail(MI_IDX_EINVAL, "plan_decode: null pointer");
@@ -327,7 +474,8 @@ extern "C" int mi_idx_plan_decode(const int32_t *seq_lens, int num_reqs, int que
     return mi_idx_fail(MI_IDX_EINVAL, "plan_decode: plan and workspace must be 16-byte aligned");
   const int cap = plan_capacity(plan_bytes);
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, seq_lens,
-                     num_reqs, max_pages, query_len, cap, (int32_t *)plan, (uint32_t *)workspace);
+                     num_reqs, max_pages, query_len, cap, query_len * num_heads, (int32_t *)plan,
+                     (uint8_t *)workspace);
   return mi_idx_check_launch("plan_decode");
 }
 
@@ -340,7 +488,7 @@ extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
                                         void *stream) {
   mi_idx_clear_error();
   int st = check_decode_sizes("score_topk_decode", num_reqs, query_len, num_heads, max_pages,
-                              plan_bytes, ws_bytes, true);
+                              plan_bytes, ws_bytes);
   if (st) return st;
   if (!(scale > 0.0f) || !std::isfinite(scale))
     return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: scale must be positive and finite");
@@ -358,13 +506,19 @@ extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
   const int cap = plan_capacity(plan_bytes);
   const int rows = query_len * num_heads;
   const int ncg = (rows + 15) / 16;
-  const dim3 grid(cap), block(64);
+  const dim3 grid((cap + 3) / 4), block(256);
   hipStream_t s = (hipStream_t)stream;
 #define MI_IDX_LAUNCH_DEC(N)                                                                   \
-  hipLaunchKernelGGL(decode_score_kernel<N>, grid, block, 0, s, q, pages, num_blocks,          \
-                     block_table, bt_stride, seq_lens, num_reqs, query_len, num_heads,         \
-                     max_pages, scale, (const int32_t *)plan, (uint8_t *)workspace, topk_out,  \
-                     scores_out)
+  if (scores_out)                                                                              \
+    hipLaunchKernelGGL((decode_score_kernel<N, true>), grid, block, 0, s, q, pages, num_blocks, \
+                       block_table, bt_stride, seq_lens, num_reqs, query_len, num_heads,       \
+                       max_pages, scale, (const int32_t *)plan, (uint8_t *)workspace,          \
+                       scores_out);                                                            \
+  else                                                                                         \
+    hipLaunchKernelGGL((decode_score_kernel<N, false>), grid, block, 0, s, q, pages,            \
+                       num_blocks, block_table, bt_stride, seq_lens, num_reqs, query_len,      \
+                       num_heads, max_pages, scale, (const int32_t *)plan,                     \
+                       (uint8_t *)workspace, scores_out)
   switch (ncg) {
     case 1: MI_IDX_LAUNCH_DEC(1); break;
     case 2: MI_IDX_LAUNCH_DEC(2); break;
@@ -372,5 +526,10 @@ extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
     default: MI_IDX_LAUNCH_DEC(4); break;
   }
 #undef MI_IDX_LAUNCH_DEC
-  return mi_idx_check_launch("score_topk_decode");
+  st = mi_idx_check_launch("score_topk_decode");
+  if (st) return st;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_reqs), dim3(256), 0, s, seq_lens, num_reqs,
+                     query_len, num_heads, max_pages, (const int32_t *)plan,
+                     (const uint8_t *)workspace, topk_out);
+  return mi_idx_check_launch("score_topk_decode (merge)");
 }

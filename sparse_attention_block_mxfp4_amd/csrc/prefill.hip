@@ -18,10 +18,8 @@ namespace mi_idx {
 
 constexpr int kTileCols = 256;          // query columns per workgroup
 constexpr int kPreHeaderInts = 16;
-constexpr int kCodeStride = 80;         // LDS bytes per token of codes (64 + pad)
-constexpr int kLdsCodes = kPageTokens * kCodeStride;        // 10240
-constexpr int kLdsScales = kPageTokens * 4;                 // 512
 constexpr int kChunks = kPageBytes / 16;                    // 544 16-byte chunks
+constexpr int kXcds = 8;                // MI355X accelerator complex dies
 
 inline int rows_per_tile(int H) { return kTileCols / H; }
 
@@ -36,8 +34,8 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     const int32_t *__restrict__ context_lens, int num_reqs, int64_t total_q, int H,
     int max_pages, float scale, const int32_t *__restrict__ plan, int32_t *__restrict__ out,
     float *__restrict__ scores_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_codes[2][kLdsCodes];
-  __shared__ __attribute__((aligned(16))) uint32_t s_scales[2][kPageTokens];
+  // Two LDS copies of a page, in its global byte layout (token t at 68*t).
+  __shared__ __attribute__((aligned(16))) uint8_t s_page[2][kPageBytes];
 
   if ((int)blockIdx.x >= plan[0]) return;
   const int4 tile = reinterpret_cast<const int4 *>(plan + kPreHeaderInts)[blockIdx.x];
@@ -87,75 +85,106 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
   TopList top;
   top.clear();
 
+  // Page pipeline.  Page p's 16-byte chunks are staged in register slot
+  // p & 1 (three chunks per thread), copied into LDS buffer p & 1, and
+  // consumed from there by all four waves.  While page j is consumed, pages
+  // j+2 and j+3 are in flight and page j+1 already sits in the other LDS
+  // buffer.  Every load is unconditional (chunk and page indices are clamped,
+  // an invalid page id reads page 0 and is skipped), and the barriers order
+  // LDS only, so the global loads stay in flight across them.
   const int32_t *bt = block_table + (int64_t)r * bt_stride;
-  uint4 pre[3];
-  auto issue = [&](int j) -> bool {
+  const int jlast = J - 1;
+  const int c2 = min(tid + 512, kChunks - 1);
+  uint4 e0, e1, e2, o0, o1, o2;   // slot 0 (even pages), slot 1 (odd pages)
+#define MI_IDX_PF_ISSUE(J_, R0, R1, R2)                                                      \
+  {                                                                                          \
+    const int phys_ = bt[min((J_), jlast)];                                                  \
+    const bool valid_ = phys_ >= 0 && (int64_t)phys_ < num_blocks;                           \
+    const uint4 *src_ =                                                                      \
+        reinterpret_cast<const uint4 *>(pages + (int64_t)(valid_ ? phys_ : 0) * kPageBytes); \
+    R0 = src_[tid];                                                                          \
+    R1 = src_[tid + 256];                                                                    \
+    R2 = src_[c2];                                                                           \
+  }
+#define MI_IDX_PF_COMMIT(BUF, R0, R1, R2)                                \
+  {                                                                      \
+    uint4 *d_ = reinterpret_cast<uint4 *>(s_page[BUF]);                  \
+    d_[tid] = R0;                                                        \
+    d_[tid + 256] = R1;                                                  \
+    if (tid + 512 < kChunks) d_[tid + 512] = R2;                         \
+  }
+  auto compute = [&](int buf, int j) {
     const int phys = bt[j];
-    if (phys < 0 || (int64_t)phys >= num_blocks) return false;
-    const uint4 *src = reinterpret_cast<const uint4 *>(pages + (int64_t)phys * kPageBytes);
+    if (phys < 0 || (int64_t)phys >= num_blocks) return;
+    const uint8_t *pg = s_page[buf];
+    u32x4 A[8];
+    uint32_t S[8];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int c = tid + 256 * k;
-      if (c < kChunks) pre[k] = src[c];
+    for (int tl = 0; tl < 8; ++tl) {
+      const uint8_t *tp = pg + (tl * 16 + t16) * kTokenBytes;
+      const u32x4a4 a4 = *reinterpret_cast<const u32x4a4 *>(tp + 16 * g);
+      A[tl] = u32x4{a4.x, a4.y, a4.z, a4.w};
+      S[tl] = tp[64 + g];
     }
-    return true;
-  };
-  auto commit = [&](int buf) {
+    float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    v4f cx[4], cy[4];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int c = tid + 256 * k;
-      if (c < kChunks) {
-        const uint32_t w4[4] = {pre[k].x, pre[k].y, pre[k].z, pre[k].w};
+    for (int cg = 0; cg < 4; ++cg) cx[cg] = mfma_fp4_fp8(A[0], bq[cg], S[0]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int w = 4 * c + i;           // dword of the page
-          const int t = w / 17, d = w - t * 17;
-          if (d < 16)
-            *reinterpret_cast<uint32_t *>(&s_codes[buf][t * kCodeStride + 4 * d]) = w4[i];
-          else
-            s_scales[buf][t] = w4[i];
-        }
+    for (int tl = 1; tl < 8; ++tl) {
+      v4f *cur = (tl & 1) ? cy : cx;
+      v4f *prev = (tl & 1) ? cx : cy;
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        cur[cg] = mfma_fp4_fp8(A[tl], bq[cg], S[tl]);
+        m[cg] = fmaxf(m[cg], max4(prev[cg]));
       }
+    }
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) m[cg] = fmaxf(m[cg], max4(cy[cg]));
+    // Reduce-scatter over the 4 lane groups: lane group g ends with the
+    // page max of its wave's column group g.
+    const bool b1 = (g >> 1) & 1, b0 = g & 1;
+    const float s0 = b1 ? m[0] : m[2], s1 = b1 ? m[1] : m[3];
+    const float k0 = fmaxf(b1 ? m[2] : m[0], __shfl_xor(s0, 32, 64));
+    const float k1 = fmaxf(b1 ? m[3] : m[1], __shfl_xor(s1, 32, 64));
+    const float sv = b0 ? k0 : k1;
+    const float v = fmaxf(b0 ? k1 : k0, __shfl_xor(sv, 16, 64));
+    if (j < myL) {
+      top.insert(make_key(v, j));
+      if (scores_out != nullptr) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
     }
   };
 
-  bool ok_cur = false;
   if (J > 0) {
-    ok_cur = issue(0);
-    if (ok_cur) commit(0);
-  }
-  __syncthreads();
-  for (int j = 0; j < J; ++j) {
-    const int buf = j & 1;
-    bool ok_nxt = false;
-    if (j + 1 < J) ok_nxt = issue(j + 1);
-    if (ok_cur) {
-      float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-      for (int tl = 0; tl < 8; ++tl) {
-        const int tok = tl * 16 + t16;
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(&s_codes[buf][tok * kCodeStride + 16 * g]);
-        const uint32_t s = (s_scales[buf][tok] >> (8 * g)) & 0xFFu;
-#pragma unroll
-        for (int cg = 0; cg < 4; ++cg) m[cg] = fmaxf(m[cg], max4(mfma_fp4_fp8(a, bq[cg], s)));
-      }
-      // Reduce-scatter over the 4 lane groups: lane group g ends with the
-      // page max of its wave's column group g.
-      const bool b1 = (g >> 1) & 1, b0 = g & 1;
-      const float s0 = b1 ? m[0] : m[2], s1 = b1 ? m[1] : m[3];
-      const float k0 = fmaxf(b1 ? m[2] : m[0], __shfl_xor(s0, 32, 64));
-      const float k1 = fmaxf(b1 ? m[3] : m[1], __shfl_xor(s1, 32, 64));
-      const float sv = b0 ? k0 : k1;
-      const float v = fmaxf(b0 ? k1 : k0, __shfl_xor(sv, 16, 64));
-      if (j < myL) {
-        top.insert(make_key(v, j));
-        if (scores_out != nullptr) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
-      }
+    MI_IDX_PF_ISSUE(0, e0, e1, e2);
+    __builtin_amdgcn_sched_barrier(0);
+    MI_IDX_PF_ISSUE(1, o0, o1, o2);
+    __builtin_amdgcn_sched_barrier(0);
+    MI_IDX_PF_COMMIT(0, e0, e1, e2);
+    __builtin_amdgcn_sched_barrier(0);
+    MI_IDX_PF_ISSUE(2, e0, e1, e2);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    for (int j = 0; j < J; j += 2) {
+      // even page j in LDS buffer 0; pages j+1 (slot 1) and j+2 (slot 0) in flight
+      MI_IDX_PF_COMMIT(1, o0, o1, o2);
+      __builtin_amdgcn_sched_barrier(0);
+      MI_IDX_PF_ISSUE(j + 3, o0, o1, o2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, j);
+      lds_barrier();
+      // odd page j+1 in LDS buffer 1; pages j+2 (slot 0) and j+3 (slot 1) in flight
+      MI_IDX_PF_COMMIT(0, e0, e1, e2);
+      __builtin_amdgcn_sched_barrier(0);
+      MI_IDX_PF_ISSUE(j + 4, e0, e1, e2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < J) compute(1, j + 1);
+      lds_barrier();
     }
-    if (ok_nxt) commit(buf ^ 1);
-    ok_cur = ok_nxt;
-    __syncthreads();
   }
+#undef MI_IDX_PF_ISSUE
+#undef MI_IDX_PF_COMMIT
   if (my_rl < nrows && myT < total_q) write_row(out + (myT * H + my_h) * kTopk, top, myL);
 }
 
@@ -227,11 +256,52 @@ extern "C" int mi_idx_plan_prefill(const int32_t *cu_seqlens_q_host, const int32
       tiles.push_back({r, row0, n, pages_ub, chunk_of[r]});
     }
   }
-  // Chunk by chunk; inside a chunk the longest tiles first.
-  std::stable_sort(tiles.begin(), tiles.end(), [](const Tile &a, const Tile &b) {
-    if (a.chunk != b.chunk) return a.chunk < b.chunk;
-    return a.pages > b.pages;
-  });
+  // Launch order.  Workgroup b runs on XCD b % kXcds, and each XCD has its
+  // own L2, so tiles that read the same pages (those of one request) should
+  // share an XCD.  Chunk by chunk: the chunk's tiles, in request order, fill
+  // the XCD queues one after another up to an equal share of the page work
+  // each; every queue is sorted longest first; the queues are interleaved so
+  // that position b takes the next tile of queue b % kXcds.
+  std::vector<Tile> order;
+  order.reserve(tiles.size());
+  {
+    size_t t0 = 0;
+    while (t0 < tiles.size()) {
+      size_t t1 = t0;
+      int64_t work = 0;
+      while (t1 < tiles.size() && tiles[t1].chunk == tiles[t0].chunk) {
+        work += (int64_t)tiles[t1].pages + 1;
+        ++t1;
+      }
+      std::vector<std::vector<Tile>> queue(kXcds);
+      const int64_t share = (work + kXcds - 1) / kXcds;
+      int x = 0;
+      int64_t filled = 0;
+      for (size_t i = t0; i < t1; ++i) {
+        if (filled >= share && x < kXcds - 1) {
+          ++x;
+          filled = 0;
+        }
+        queue[x].push_back(tiles[i]);
+        filled += (int64_t)tiles[i].pages + 1;
+      }
+      for (auto &qx : queue)
+        std::stable_sort(qx.begin(), qx.end(),
+                         [](const Tile &a, const Tile &b) { return a.pages > b.pages; });
+      std::vector<size_t> head(kXcds, 0);
+      size_t left = t1 - t0;
+      int xi = (int)(order.size() % kXcds);   // the XCD of the next position
+      while (left > 0) {
+        if (head[xi] < queue[xi].size()) {
+          order.push_back(queue[xi][head[xi]++]);
+          --left;
+        }
+        xi = (xi + 1) % kXcds;
+      }
+      t0 = t1;
+    }
+  }
+  tiles.swap(order);
   int32_t *st = static_cast<int32_t *>(staging_host_pinned);
   const size_t bytes = (size_t)kPreHeaderInts * 4 + tiles.size() * 16;
   if (bytes > plan_bytes)

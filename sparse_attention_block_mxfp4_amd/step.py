@@ -59,8 +59,8 @@ class IndexerStep:
              prefill_seq_lens_host=None, gather_budget_pages=0, stream=None):
         """decode_seq_lens: device int32 [Rd]; prefill lengths: host arrays."""
         if decode_seq_lens is not None and decode_seq_lens.numel() > 0:
-            mi_idx_plan_decode(decode_seq_lens, self.query_len, self.max_pages, self.dec_plan,
-                               self.dec_ws, stream=stream)
+            mi_idx_plan_decode(decode_seq_lens, self.query_len, self.H, self.max_pages,
+                               self.dec_plan, self.dec_ws, stream=stream)
         self.num_tiles = 0
         if prefill_cu_seqlens_q_host is not None and len(prefill_seq_lens_host) > 0:
             k = self._next_staging

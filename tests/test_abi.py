@@ -49,8 +49,8 @@ def test_version_and_reason(m):
 
 
 def test_sizes(m):
-    assert m.mi_idx_decode_plan_bytes(64) == 64 + (64 + 2048) * 32
-    assert m.mi_idx_decode_workspace_bytes(64, 1, 1) == 256 + 256 + (64 + 2048) * 15 * 8
+    assert m.mi_idx_decode_plan_bytes(64) == 64 + (64 + 2048) * 16
+    assert m.mi_idx_decode_workspace_bytes(64, 1, 1) == 256 + (64 + 2048) * 16 * 8 + 8 * 64
     assert m.mi_idx_decode_workspace_bytes(0, 0, 1) == 0
     assert m.mi_idx_prefill_plan_bytes(8, 32768, 4) == 64 + (32768 // 64 + 8 + 1) * 16
     assert m.mi_idx_prefill_plan_bytes(1, 10, 9) == 0
@@ -91,10 +91,12 @@ def test_decode_argument_errors(m):
     assert call(q=buf + 4) == m.EINVAL          # misaligned
     assert b"scale" in L.mi_idx_last_error() or True
     assert call(R=0) == m.OK                    # nothing to do, nothing launched
-    assert L.mi_idx_plan_decode(buf, 4, 9, 16, P, pb, W, wb, None) == m.EUNSUPPORTED
-    assert L.mi_idx_plan_decode(buf, 5, 2, 16, P, pb, W, wb, None) == m.ECAPACITY
-    assert L.mi_idx_plan_decode(None, 4, 2, 16, P, pb, W, wb, None) == m.EINVAL
-    assert L.mi_idx_plan_decode(buf, 4, 2, -1, P, pb, W, wb, None) == m.EINVAL
+    assert L.mi_idx_plan_decode(buf, 4, 9, 2, 16, P, pb, W, wb, None) == m.EUNSUPPORTED
+    assert L.mi_idx_plan_decode(buf, 4, 2, 9, 16, P, pb, W, wb, None) == m.EUNSUPPORTED
+    assert L.mi_idx_plan_decode(buf, 5, 2, 2, 16, P, pb, W, wb, None) == m.ECAPACITY
+    assert L.mi_idx_plan_decode(buf, 4, 2, 4, 16, P, pb, W, wb, None) == m.ECAPACITY
+    assert L.mi_idx_plan_decode(None, 4, 2, 2, 16, P, pb, W, wb, None) == m.EINVAL
+    assert L.mi_idx_plan_decode(buf, 4, 2, 2, -1, P, pb, W, wb, None) == m.EINVAL
     assert len(L.mi_idx_last_error()) > 0
 
 
@@ -178,6 +180,7 @@ def test_prefill_host_plan_matches_oracle_chunking(m, H):
             cover[r][row0:row0 + nr] += 1
             assert pages == max((sl[r] - qn[r] + row0 + nr - 1) // 128, 0)
         assert all(np.all(c == 1) for c in cover)
-        # chunk order, then longest first
-        key = [(chunk_of[r], -pages) for r, _, _, pages in t]
-        assert key == sorted(key)
+        # chunks are launched in order (the tile order inside a chunk is a
+        # placement choice and is not part of the contract)
+        ch_seq = [chunk_of[r] for r, _, _, _ in t]
+        assert ch_seq == sorted(ch_seq)
