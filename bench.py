@@ -75,6 +75,23 @@ def algorithmic(w):
                 pre_bytes=pre_bytes, pre_pages=pre_pages)
 
 
+def measured_traffic(kernel, source):
+    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, scaled by the
+    copy calibration) from the committed rocprofv3 summary, or None when the
+    kernel's source has changed since the counters were taken."""
+    import hashlib
+    summary = os.path.join(ROOT, "profiles", "mixed_step_kernels.txt")
+    src = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc", source)
+    if not (os.path.exists(summary) and os.path.exists(src)):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(summary):
+        f = line.split()
+        if len(f) == 4 and f[0] == kernel and f[3] == digest:
+            return int(float(f[1]) + float(f[2]))
+    return None
+
+
 def cpu_baseline(w):
     """The oracle on a bounded sample: two whole decode requests and 512 rows
     of one prefill request, scoring + selection only (pages encoded before
@@ -226,11 +243,13 @@ def main():
                     "rows_per_s": round(w.n_prefill_rows / (pre_ms * 1e-3), 1) if w.Rp else None},
     }
     roof_dec = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                "kernel": "decode_score_kernel"}
+                "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                "traffic": measured_traffic("decode_score_kernel", "decode.hip"),
+                "kernel": "decode_score_kernel + decode_merge_kernel"}
     roof_pre = {"bound": "mfma", "achieved": round(pre_tflops, 1), "peak": PEAK_FP8_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_FP8_TFLOPS, 4),
-                "traffic": None, "kernel": "prefill_score_kernel"}
+                "traffic": measured_traffic("prefill_score_kernel", "prefill.hip"),
+                "kernel": "prefill_score_kernel"}
     dominant = roof_pre if (w.Rp and pre_ms >= dec_ms) else roof_dec
     res = {
         "metric": METRIC,

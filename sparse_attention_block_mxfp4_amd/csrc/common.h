@@ -42,6 +42,11 @@ __device__ __forceinline__ float max4(const v4f &c) {
   return fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w));
 }
 
+// m = max(m, c.x, c.y, c.z, c.w) as two 3-input maxima.
+__device__ __forceinline__ float fold4(float m, const v4f &c) {
+  return fmaxf(fmaxf(fmaxf(fmaxf(m, c.x), c.y), c.z), c.w);
+}
+
 // Selection key: larger is better.  High word = the score's bits mapped to
 // an unsigned order (NaN lowest, -0 folded into +0); low word = ~id so that
 // equal scores prefer the lower id.  0 is "empty" (below every real key).
@@ -69,6 +74,17 @@ struct TopList {
     for (int i = 0; i < kHist; ++i) k[i] = 0ull;
   }
   __device__ __forceinline__ uint64_t threshold() const { return k[kHist - 1]; }
+  // Insert x with no branch (x = 0 leaves the list unchanged), so the caller's
+  // basic block stays whole for the scheduler.
+  __device__ __forceinline__ void insert_nb(uint64_t x) {
+#pragma unroll
+    for (int i = 0; i < kHist; ++i) {
+      const uint64_t hi = k[i] > x ? k[i] : x;
+      const uint64_t lo = k[i] > x ? x : k[i];
+      k[i] = hi;
+      x = lo;
+    }
+  }
   // Insert x (no-op when x does not beat the current 15th key).
   __device__ __forceinline__ void insert(uint64_t x) {
     if (x <= k[kHist - 1]) return;
@@ -79,6 +95,65 @@ struct TopList {
       k[i] = hi;
       x = lo;
     }
+  }
+};
+
+// Max of v over lanes l and l^32 (resp. l^16), through gfx950's VALU lane
+// swaps: for every lane the swap returns {own, partner} in some order.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Lanes 0..31 get max(a, a of lane+32), lanes 32..63 get max(b, b of lane-32).
+__device__ __forceinline__ float max_split32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Even 16-lane rows get max(a, a of the next row), odd rows get max(b, b of
+// the previous row).
+__device__ __forceinline__ float max_split16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// A top-15 list with a 4-slot per-lane pending buffer: a key that beats the
+// list's current 15th key is shifted into the buffer (a few selects, no
+// branch); when any lane of the wave has a full buffer, every lane's buffer
+// is inserted into its list.  Early on almost every page qualifies, later
+// only a few, so most pages cost ~10 VALU instead of a full insertion.
+struct PendingTop {
+  TopList top;
+  uint64_t p0, p1, p2, p3;
+  int n;
+  __device__ __forceinline__ void clear() {
+    top.clear();
+    p0 = p1 = p2 = p3 = 0ull;
+    n = 0;
+  }
+  __device__ __forceinline__ void flush() {
+    top.insert_nb(p0);
+    top.insert_nb(p1);
+    top.insert_nb(p2);
+    top.insert_nb(p3);
+    p0 = p1 = p2 = p3 = 0ull;
+    n = 0;
+  }
+  __device__ __forceinline__ void push(uint64_t key) {
+    const bool c = key > top.k[kHist - 1];
+    p3 = c ? p2 : p3;
+    p2 = c ? p1 : p2;
+    p1 = c ? p0 : p1;
+    p0 = c ? key : p0;
+    n += c ? 1 : 0;
+    if (__any(n == 4)) flush();
   }
 };
 

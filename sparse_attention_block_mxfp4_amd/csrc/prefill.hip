@@ -20,6 +20,10 @@ constexpr int kTileCols = 256;          // query columns per workgroup
 constexpr int kPreHeaderInts = 16;
 constexpr int kChunks = kPageBytes / 16;                    // 544 16-byte chunks
 constexpr int kXcds = 8;                // MI355X accelerator complex dies
+#ifndef MI_IDX_PREFILL_CGW
+#define MI_IDX_PREFILL_CGW 4
+#endif
+constexpr int kPrefillCgw = MI_IDX_PREFILL_CGW;   // 16-column groups per wave
 
 inline int rows_per_tile(int H) { return kTileCols / H; }
 
@@ -27,14 +31,38 @@ inline int rows_per_tile(int H) { return kTileCols / H; }
 // [3] chunk count.  Tile (int4): request, first row (in the request), row
 // count, page upper bound.
 
-__global__ __launch_bounds__(256) void prefill_score_kernel(
+// Token of a page that MFMA row t16 of tile tl reads.  A page's score is a
+// max over its tokens, so any assignment that covers the 128 tokens once is
+// correct; the one chosen spreads a tile's LDS reads (dword 17*token + 4*g)
+// over distinct banks.
+#ifndef MI_IDX_TOKEN_MAP
+#define MI_IDX_TOKEN_MAP 32
+#endif
+__device__ __forceinline__ int page_token(int tl, int t16) {
+#if MI_IDX_TOKEN_MAP == 64
+  return 64 * (tl >> 2) + 16 * (t16 >> 2) + 4 * (tl & 3) + (t16 & 3);
+#elif MI_IDX_TOKEN_MAP == 32
+  return 32 * (tl >> 1) + 8 * (t16 >> 2) + 4 * (tl & 1) + (t16 & 3);
+#else
+  return tl * 16 + t16;
+#endif
+}
+
+// CGW = 16-column MFMA groups per wave; the workgroup has 16 / CGW waves
+// and always covers kTileCols = 256 query columns.
+template <int CGW, bool kScores>
+__global__ __launch_bounds__(64 * (16 / CGW)) void prefill_score_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ pages, int64_t num_blocks,
     const int32_t *__restrict__ block_table, int64_t bt_stride,
     const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ context_lens, int num_reqs, int64_t total_q, int H,
     int max_pages, float scale, const int32_t *__restrict__ plan, int32_t *__restrict__ out,
     float *__restrict__ scores_out) {
-  // Two LDS copies of a page, in its global byte layout (token t at 68*t).
+  constexpr int NW = 16 / CGW;                       // waves per workgroup
+  constexpr int NT = 64 * NW;                        // threads per workgroup
+  constexpr int kLoads = (kChunks + NT - 1) / NT;    // 16-byte chunks per thread
+  // Two LDS page buffers, each in the page's global byte layout (token t at
+  // 68*t).
   __shared__ __attribute__((aligned(16))) uint8_t s_page[2][kPageBytes];
 
   if ((int)blockIdx.x >= plan[0]) return;
@@ -48,11 +76,11 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
   const int sl = seq_lens[r];
   const int64_t q0 = cu_seqlens_q[r];
 
-  // B operands: columns (wave*4 + cg)*16 + t16.
-  v8i bq[4];
+  // B operands: columns (wave*CGW + cg)*16 + t16.
+  v8i bq[CGW];
 #pragma unroll
-  for (int cg = 0; cg < 4; ++cg) {
-    const int col = (wave * 4 + cg) * 16 + t16;
+  for (int cg = 0; cg < CGW; ++cg) {
+    const int col = (wave * CGW + cg) * 16 + t16;
     const int rl = col / H, h = col - rl * H;
     bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     if (rl < nrows) {
@@ -66,8 +94,12 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
       }
     }
   }
-  // The column this lane owns after the reduce-scatter: group g of this wave.
-  const int mycol = (wave * 4 + g) * 16 + t16;
+  // The column this lane owns after the page-max reduction: with 4 groups
+  // per wave each lane group owns one; with 2, lane groups g and g^1 both
+  // hold group g>>1 (the even one writes it); with 1, all hold it.
+  const int my_cg = CGW == 4 ? g : (CGW == 2 ? (g >> 1) : 0);
+  const bool writer = CGW == 4 ? true : (CGW == 2 ? (g & 1) == 0 : g == 0);
+  const int mycol = (wave * CGW + my_cg) * 16 + t16;
   const int my_rl = mycol / H, my_h = mycol - my_rl * H;
   const int64_t myT = q0 + row0 + my_rl;
   int myL = -1;
@@ -82,110 +114,120 @@ __global__ __launch_bounds__(256) void prefill_score_kernel(
     J = plast >= 0 ? min(plast >> 7, max_pages) : 0;
     J = max(J, 0);
   }
-  TopList top;
+  PendingTop top;
   top.clear();
 
   // Page pipeline.  Page p's 16-byte chunks are staged in register slot
-  // p & 1 (three chunks per thread), copied into LDS buffer p & 1, and
-  // consumed from there by all four waves.  While page j is consumed, pages
+  // p & 1 (kLoads chunks per thread), copied into LDS buffer p & 1, and
+  // consumed from there by all the waves.  While page j is consumed, pages
   // j+2 and j+3 are in flight and page j+1 already sits in the other LDS
   // buffer.  Every load is unconditional (chunk and page indices are clamped,
   // an invalid page id reads page 0 and is skipped), and the barriers order
   // LDS only, so the global loads stay in flight across them.
   const int32_t *bt = block_table + (int64_t)r * bt_stride;
   const int jlast = J - 1;
-  const int c2 = min(tid + 512, kChunks - 1);
-  uint4 e0, e1, e2, o0, o1, o2;   // slot 0 (even pages), slot 1 (odd pages)
-#define MI_IDX_PF_ISSUE(J_, R0, R1, R2)                                                      \
-  {                                                                                          \
-    const int phys_ = bt[min((J_), jlast)];                                                  \
-    const bool valid_ = phys_ >= 0 && (int64_t)phys_ < num_blocks;                           \
-    const uint4 *src_ =                                                                      \
-        reinterpret_cast<const uint4 *>(pages + (int64_t)(valid_ ? phys_ : 0) * kPageBytes); \
-    R0 = src_[tid];                                                                          \
-    R1 = src_[tid + 256];                                                                    \
-    R2 = src_[c2];                                                                           \
-  }
-#define MI_IDX_PF_COMMIT(BUF, R0, R1, R2)                                \
-  {                                                                      \
-    uint4 *d_ = reinterpret_cast<uint4 *>(s_page[BUF]);                  \
-    d_[tid] = R0;                                                        \
-    d_[tid + 256] = R1;                                                  \
-    if (tid + 512 < kChunks) d_[tid + 512] = R2;                         \
-  }
-  auto compute = [&](int buf, int j) {
-    const int phys = bt[j];
-    if (phys < 0 || (int64_t)phys >= num_blocks) return;
+  static_assert(kLoads >= 1 && kLoads <= 3, "page staging takes 1..3 chunks per thread");
+  // slot 0 (even pages): e0..e2, slot 1 (odd pages): o0..o2
+  uint4 e0, e1, e2, o0, o1, o2;
+  auto pf_issue = [&](int jj, uint4 &R0, uint4 &R1, uint4 &R2) {
+    const int phys = bt[min(jj, jlast)];
+    const bool valid = phys >= 0 && (int64_t)phys < num_blocks;
+    const uint4 *src =
+        reinterpret_cast<const uint4 *>(pages + (int64_t)(valid ? phys : 0) * kPageBytes);
+    R0 = src[min(tid, kChunks - 1)];
+    if (kLoads > 1) R1 = src[min(tid + NT, kChunks - 1)];
+    if (kLoads > 2) R2 = src[min(tid + 2 * NT, kChunks - 1)];
+  };
+  auto pf_commit = [&](int buf, const uint4 &R0, const uint4 &R1, const uint4 &R2) {
+    uint4 *d = reinterpret_cast<uint4 *>(s_page[buf]);
+    if (tid < kChunks) d[tid] = R0;
+    if (kLoads > 1 && tid + NT < kChunks) d[tid + NT] = R1;
+    if (kLoads > 2 && tid + 2 * NT < kChunks) d[tid + 2 * NT] = R2;
+  };
+  // Page max of every column of the wave for the page in LDS buffer buf:
+  // 8 token tiles x CGW MFMAs, tile tl's MFMAs into one accumulator set while
+  // tile tl-1's are folded into the maxima, then the reduction over the 4
+  // lane groups (token quarters) with VALU lane swaps.  No branches.
+  auto page_max = [&](int buf) -> float {
     const uint8_t *pg = s_page[buf];
     u32x4 A[8];
     uint32_t S[8];
 #pragma unroll
     for (int tl = 0; tl < 8; ++tl) {
-      const uint8_t *tp = pg + (tl * 16 + t16) * kTokenBytes;
+      const uint8_t *tp = pg + page_token(tl, t16) * kTokenBytes;
       const u32x4a4 a4 = *reinterpret_cast<const u32x4a4 *>(tp + 16 * g);
       A[tl] = u32x4{a4.x, a4.y, a4.z, a4.w};
       S[tl] = tp[64 + g];
     }
-    float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    v4f cx[4], cy[4];
+    float m[CGW];
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) cx[cg] = mfma_fp4_fp8(A[0], bq[cg], S[0]);
+    for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
+    v4f cx[CGW], cy[CGW];
+#pragma unroll
+    for (int cg = 0; cg < CGW; ++cg) cx[cg] = mfma_fp4_fp8(A[0], bq[cg], S[0]);
 #pragma unroll
     for (int tl = 1; tl < 8; ++tl) {
-      v4f *cur = (tl & 1) ? cy : cx;
-      v4f *prev = (tl & 1) ? cx : cy;
 #pragma unroll
-      for (int cg = 0; cg < 4; ++cg) {
-        cur[cg] = mfma_fp4_fp8(A[tl], bq[cg], S[tl]);
-        m[cg] = fmaxf(m[cg], max4(prev[cg]));
+      for (int cg = 0; cg < CGW; ++cg) {
+        if (tl & 1) {
+          cy[cg] = mfma_fp4_fp8(A[tl], bq[cg], S[tl]);
+          m[cg] = fold4(m[cg], cx[cg]);
+        } else {
+          cx[cg] = mfma_fp4_fp8(A[tl], bq[cg], S[tl]);
+          m[cg] = fold4(m[cg], cy[cg]);
+        }
       }
     }
 #pragma unroll
-    for (int cg = 0; cg < 4; ++cg) m[cg] = fmaxf(m[cg], max4(cy[cg]));
-    // Reduce-scatter over the 4 lane groups: lane group g ends with the
-    // page max of its wave's column group g.
-    const bool b1 = (g >> 1) & 1, b0 = g & 1;
-    const float s0 = b1 ? m[0] : m[2], s1 = b1 ? m[1] : m[3];
-    const float k0 = fmaxf(b1 ? m[2] : m[0], __shfl_xor(s0, 32, 64));
-    const float k1 = fmaxf(b1 ? m[3] : m[1], __shfl_xor(s1, 32, 64));
-    const float sv = b0 ? k0 : k1;
-    const float v = fmaxf(b0 ? k1 : k0, __shfl_xor(sv, 16, 64));
-    if (j < myL) {
-      top.insert(make_key(v, j));
-      if (scores_out != nullptr) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
+    for (int cg = 0; cg < CGW; ++cg) m[cg] = fold4(m[cg], cy[cg]);
+    if constexpr (CGW == 4) {
+      // reduce-scatter: lane group g ends with column group g's max
+      const float k0 = max_split32(m[0], m[2]);   // groups 0,1: cg 0; groups 2,3: cg 2
+      const float k1 = max_split32(m[1], m[3]);   // groups 0,1: cg 1; groups 2,3: cg 3
+      return max_split16(k0, k1);                 // group g: cg g
+    } else if constexpr (CGW == 2) {
+      return max_xor16(max_split32(m[0], m[1]));  // groups 0,1: cg 0; 2,3: cg 1
+    } else {
+      return max_xor16(max_xor32(m[0]));
     }
+  };
+  auto take = [&](float v, int j) {
+    const int phys = bt[min(j, jlast)];
+    const bool ok = j < myL && phys >= 0 && (int64_t)phys < num_blocks;
+    top.push(ok ? make_key(v, j) : 0ull);
+    if (kScores && writer && ok) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
   };
 
   if (J > 0) {
-    MI_IDX_PF_ISSUE(0, e0, e1, e2);
+    pf_issue(0, e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
-    MI_IDX_PF_ISSUE(1, o0, o1, o2);
+    pf_issue(1, o0, o1, o2);
     __builtin_amdgcn_sched_barrier(0);
-    MI_IDX_PF_COMMIT(0, e0, e1, e2);
+    pf_commit(0, e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
-    MI_IDX_PF_ISSUE(2, e0, e1, e2);
+    pf_issue(2, e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     for (int j = 0; j < J; j += 2) {
       // even page j in LDS buffer 0; pages j+1 (slot 1) and j+2 (slot 0) in flight
-      MI_IDX_PF_COMMIT(1, o0, o1, o2);
+      pf_commit(1, o0, o1, o2);
       __builtin_amdgcn_sched_barrier(0);
-      MI_IDX_PF_ISSUE(j + 3, o0, o1, o2);
+      pf_issue(j + 3, o0, o1, o2);
       __builtin_amdgcn_sched_barrier(0);
-      compute(0, j);
+      take(page_max(0), j);
       lds_barrier();
       // odd page j+1 in LDS buffer 1; pages j+2 (slot 0) and j+3 (slot 1) in flight
-      MI_IDX_PF_COMMIT(0, e0, e1, e2);
+      pf_commit(0, e0, e1, e2);
       __builtin_amdgcn_sched_barrier(0);
-      MI_IDX_PF_ISSUE(j + 4, e0, e1, e2);
+      pf_issue(j + 4, e0, e1, e2);
       __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 < J) compute(1, j + 1);
+      take(page_max(1), j + 1);
       lds_barrier();
     }
   }
-#undef MI_IDX_PF_ISSUE
-#undef MI_IDX_PF_COMMIT
-  if (my_rl < nrows && myT < total_q) write_row(out + (myT * H + my_h) * kTopk, top, myL);
+  top.flush();
+  if (writer && my_rl < nrows && myT < total_q)
+    write_row(out + (myT * H + my_h) * kTopk, top.top, myL);
 }
 
 }  // namespace mi_idx
@@ -357,9 +399,16 @@ extern "C" int mi_idx_score_topk_prefill(const uint8_t *q, const uint8_t *pages,
   if ((size_t)kPreHeaderInts * 4 + (size_t)num_tiles * 16 > plan_bytes)
     return mi_idx_fail(MI_IDX_ECAPACITY, "score_topk_prefill: num_tiles %d exceeds plan_bytes",
                        num_tiles);
-  hipLaunchKernelGGL(prefill_score_kernel, dim3(num_tiles), dim3(256), 0, (hipStream_t)stream, q,
-                     pages, num_blocks, block_table, bt_stride, cu_seqlens_q, seq_lens,
-                     context_lens, num_reqs, total_q, num_heads, max_pages, scale,
-                     (const int32_t *)plan, topk_out, scores_out);
+  const dim3 grid(num_tiles), block(64 * (16 / kPrefillCgw));
+  if (scores_out)
+    hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, true>), grid, block, 0,
+                       (hipStream_t)stream, q, pages, num_blocks, block_table, bt_stride,
+                       cu_seqlens_q, seq_lens, context_lens, num_reqs, total_q, num_heads,
+                       max_pages, scale, (const int32_t *)plan, topk_out, scores_out);
+  else
+    hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, false>), grid, block, 0,
+                       (hipStream_t)stream, q, pages, num_blocks, block_table, bt_stride,
+                       cu_seqlens_q, seq_lens, context_lens, num_reqs, total_q, num_heads,
+                       max_pages, scale, (const int32_t *)plan, topk_out, scores_out);
   return mi_idx_check_launch("score_topk_prefill");
 }
