@@ -31,15 +31,15 @@ constexpr int kItemInts = 4;
 constexpr size_t kWsHeaderBytes = 256;
 constexpr int kListKeys = 16;         // 15 keys + an empty slot: 128-byte lists
 constexpr int kDepth = 3;             // pages in flight per wave (register ring)
-constexpr int kMergeKeys = 2048;      // LDS keys for the bounds of one merge pass
+constexpr int kMergeKeys = 2048;      // LDS head keys of one merge pass
 constexpr int kCandKeys = 2048;       // LDS candidate keys of one merge pass
 constexpr int kMaxItemsPerReq = 256;  // bounds the merge's O(n^2) ranking
 
 // Plan header (int32): [0] item count, [1] chunk pages, [2] num_reqs,
 // [3] query_len, [4] max_pages, [5] capacity.  Items follow (int4 each).
-// Workspace: [0, 256) header (word 0: error bits), then the item lists
-// [capacity][rows][kListKeys] uint64, then (first item, item count) int2 per
-// request.
+// Workspace: [0, 256) header (word 0: error bits), then (first item, item
+// count) int2 per request, padded to 256 bytes, then the item lists
+// [capacity][rows][kListKeys] uint64.
 
 __host__ __device__ inline size_t decode_capacity(int max_reqs) {
   return (size_t)max_reqs + kTargetItems;
@@ -47,6 +47,10 @@ __host__ __device__ inline size_t decode_capacity(int max_reqs) {
 
 __host__ __device__ inline size_t lists_bytes(size_t capacity, int rows) {
   return capacity * (size_t)rows * kListKeys * 8;
+}
+
+__host__ __device__ inline size_t lists_offset(int num_reqs) {
+  return kWsHeaderBytes + (((size_t)8 * num_reqs + 255) & ~(size_t)255);
 }
 
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *__restrict__ seq_lens,
@@ -58,7 +62,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *__rest
   __shared__ int s_chunk;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
-  int2 *req_info = reinterpret_cast<int2 *>(ws + kWsHeaderBytes + lists_bytes(capacity, rows));
+  int2 *req_info = reinterpret_cast<int2 *>(ws + kWsHeaderBytes);
   // Contiguous segment of requests per thread.
   const int per = (num_reqs + nt - 1) / nt;
   const int r0 = min(num_reqs, tid * per), r1 = min(num_reqs, r0 + per);
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   const int t16 = lane & 15, g = lane >> 4;
   const int rows = query_len * H;
   const int sl = seq_lens[r];
-  uint64_t *lists = reinterpret_cast<uint64_t *>(ws + kWsHeaderBytes);
+  uint64_t *lists = reinterpret_cast<uint64_t *>(ws + lists_offset(num_reqs));
 
   // Query fragments (B operand) and the causal bound of each column.
   v8i bq[NCG];
@@ -266,8 +270,10 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   }
 }
 
+constexpr int kHead = 4;              // keys per list the merge reads up front
+
 struct MergeSmem {
-  uint64_t t[kMergeKeys];     // the lists' top keys
+  uint64_t head[kMergeKeys];  // the lists' first kHead keys
   uint64_t cand[kCandKeys];   // keys at or above a column's bound
   uint64_t thr[64];
   uint32_t ncand[64];
@@ -280,26 +286,25 @@ struct MergeSmem {
 // Any 15 distinct keys bound the 15th best key of the union from below; the
 // 15th largest of the lists' top-K keys (K = ceil(15 / n), so 1 once there
 // are 15 lists or more) is such a bound, and every key of the final top-15
-// is at or above it.  The keys at or above the bound are gathered and ranked by
-// counting (keys are distinct).  Columns go in batches that fit the LDS
-// arrays; a column whose candidates overflow its share is merged by
+// is at or above it.  The keys at or above the bound are gathered and ranked
+// by counting (keys are distinct).  The first kHead keys of every list come
+// in with two 16-byte loads; deeper keys are read only from a list whose
+// kHead-th key still reaches the bound.  Columns go in batches that fit the
+// LDS arrays; a column whose candidates overflow its share is merged by
 // per-lane insertion and a butterfly instead (slower, same result).
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int32_t *__restrict__ seq_lens, int num_reqs, int query_len, int H, int max_pages,
-    const int32_t *__restrict__ plan, const uint8_t *__restrict__ ws,
-    int32_t *__restrict__ out) {
+    const uint8_t *__restrict__ ws, int32_t *__restrict__ out) {
   __shared__ MergeSmem sm;
   const int r = blockIdx.x;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int rows = query_len * H;
-  const int capacity = plan[5];
-  const uint64_t *lists = reinterpret_cast<const uint64_t *>(ws + kWsHeaderBytes);
-  const int2 info = reinterpret_cast<const int2 *>(ws + kWsHeaderBytes +
-                                                   lists_bytes(capacity, rows))[r];
+  const uint64_t *lists = reinterpret_cast<const uint64_t *>(ws + lists_offset(num_reqs));
+  const int2 info = reinterpret_cast<const int2 *>(ws + kWsHeaderBytes)[r];
   const int first = info.x, n = info.y;
   const int sl = seq_lens[r];
-  auto key = [&](int c, int x, int k) -> uint64_t {
-    return lists[((size_t)(first + x) * rows + c) * kListKeys + k];
+  auto list_ptr = [&](int c, int x) -> const uint64_t * {
+    return lists + ((size_t)(first + x) * rows + c) * kListKeys;
   };
   auto emit = [&](int c, int slot, uint64_t v) {
     const int qi = c / H, h = c - (c / H) * H;
@@ -308,17 +313,22 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     const int L = p >= 0 ? min(p >> 7, max_pages) : -1;
     out[(T * H + h) * kTopk + slot] = (L >= 0 && v != 0ull) ? key_id(v) : -1;
   };
-  const int K = n >= kHist ? 1 : (kHist + n - 1) / max(n, 1);
-  const int per_col = max(n * K, 1);
+  const int K = n >= kHist ? 1 : min(kHead, (kHist + n - 1) / max(n, 1));
+  const int per_col = max(n * kHead, 1);
   const int batch = max(1, min(rows, min(kMergeKeys / per_col, 64)));
   for (int c0 = 0; c0 < rows; c0 += batch) {
     const int nc = min(batch, rows - c0);
     const int cand_cap = kCandKeys / nc;
-    // 1. every list's top-K keys
-    for (int p = tid; p < nc * per_col; p += nt) {
-      const int cl = p / per_col, i = p - cl * per_col;
-      const int x = i / K, k = i - x * K;
-      sm.t[p] = n > 0 ? key(c0 + cl, x, k) : 0ull;
+    // 1. the first kHead keys of every list
+    for (int p = tid; p < nc * n; p += nt) {
+      const int cl = p / n, x = p - cl * n;
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(list_ptr(c0 + cl, x));
+      const u32x4 a = src[0], b = src[1];
+      uint64_t *h = sm.head + (size_t)p * kHead;
+      h[0] = ((uint64_t)a.y << 32) | a.x;
+      h[1] = ((uint64_t)a.w << 32) | a.z;
+      h[2] = ((uint64_t)b.y << 32) | b.x;
+      h[3] = ((uint64_t)b.w << 32) | b.z;
     }
     for (int c = tid; c < nc; c += nt) {
       sm.thr[c] = 0ull;
@@ -326,45 +336,37 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
       sm.over[c] = 0u;
     }
     __syncthreads();
-    // 2. the bound: the 15th largest of those keys (none if fewer than 15)
-    for (int p = tid; p < nc * per_col; p += nt) {
-      const int cl = p / per_col;
-      const uint64_t me = sm.t[p];
+    // 2. the bound: the 15th largest of the lists' top-K keys (none if
+    // there are fewer than 15 of them)
+    for (int p = tid; p < nc * n * K; p += nt) {
+      const int cl = p / (n * K), i = p - cl * (n * K);
+      const uint64_t *hc = sm.head + (size_t)cl * n * kHead;
+      const uint64_t me = hc[(i / K) * kHead + i % K];
       if (me == 0ull) continue;
-      const uint64_t *row = sm.t + cl * per_col;
       int rank = 0;
-      for (int i = 0; i < per_col; ++i) rank += row[i] > me ? 1 : 0;
+      for (int x = 0; x < n; ++x)
+        for (int k = 0; k < K; ++k) rank += hc[x * kHead + k] > me ? 1 : 0;
       if (rank == kHist - 1) sm.thr[cl] = me;
     }
     __syncthreads();
-    // 3. gather every key at or above the bound: the top-K keys from LDS,
-    // deeper keys from the list only when its K-th key reaches the bound
+    // 3. gather every key at or above the bound
     for (int p = tid; p < nc * n; p += nt) {
       const int cl = p / n, x = p - cl * n;
       const uint64_t thr = sm.thr[cl] ? sm.thr[cl] : 1ull;
-      const uint64_t *tk = sm.t + cl * per_col + x * K;
+      const uint64_t *h = sm.head + (size_t)p * kHead;
       int k = 0;
-      for (; k < K; ++k) {
-        const uint64_t v = tk[k];
+      for (; k < kHead; ++k) {
+        const uint64_t v = h[k];
         if (v < thr) break;
         const uint32_t pos = atomicAdd(&sm.ncand[cl], 1u);
         if (pos < (uint32_t)cand_cap) sm.cand[cl * cand_cap + pos] = v;
         else sm.over[cl] = 1u;
       }
-      // deeper keys, two per 16-byte load, while they reach the bound
-      bool more = k == K;
-      for (int k2 = K & ~1; more && k2 < kListKeys; k2 += 2) {
-        const u32x4 v4 = *reinterpret_cast<const u32x4 *>(
-            lists + ((size_t)(first + x) * rows + c0 + cl) * kListKeys + k2);
-        const uint64_t pair[2] = {((uint64_t)v4.y << 32) | v4.x, ((uint64_t)v4.w << 32) | v4.z};
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          if (k2 + e < k || !more) continue;
-          const uint64_t v = pair[e];
-          if (k2 + e >= kHist || v < thr) {
-            more = false;
-            continue;
-          }
+      if (k == kHead) {
+        const uint64_t *src = list_ptr(c0 + cl, x);
+        for (; k < kHist; ++k) {
+          const uint64_t v = src[k];
+          if (v < thr) break;
           const uint32_t pos = atomicAdd(&sm.ncand[cl], 1u);
           if (pos < (uint32_t)cand_cap) sm.cand[cl * cand_cap + pos] = v;
           else sm.over[cl] = 1u;
@@ -394,8 +396,9 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
         TopList acc;
         acc.clear();
         for (int x = tid; x < n; x += 64) {
+          const uint64_t *src = list_ptr(c0 + cl, x);
           for (int k = 0; k < kHist; ++k) {
-            const uint64_t v = key(c0 + cl, x, k);
+            const uint64_t v = src[k];
             if (v <= acc.threshold()) break;
             acc.insert(v);
           }
@@ -432,8 +435,7 @@ extern "C" size_t mi_idx_decode_plan_bytes(int max_reqs) {
 
 extern "C" size_t mi_idx_decode_workspace_bytes(int max_reqs, int query_len, int num_heads) {
   if (max_reqs < 0 || query_len < 1 || num_heads < 1) return 0;
-  return kWsHeaderBytes + lists_bytes(decode_capacity(max_reqs), query_len * num_heads) +
-         (size_t)8 * max_reqs;
+  return lists_offset(max_reqs) + lists_bytes(decode_capacity(max_reqs), query_len * num_heads);
 }
 
 static int plan_capacity(size_t plan_bytes) {
@@ -454,8 +456,7 @@ static int check_decode_sizes(const char *who, int num_reqs, int query_len, int 
   if ((size_t)cap < decode_capacity(num_reqs))
     return mi_idx_fail(MI_IDX_ECAPACITY, "%s: plan_bytes %zu < %zu needed for %d requests", who,
                        plan_bytes, mi_idx_decode_plan_bytes(num_reqs), num_reqs);
-  const size_t need =
-      kWsHeaderBytes + lists_bytes(cap, query_len * num_heads) + (size_t)8 * num_reqs;
+  const size_t need = lists_offset(num_reqs) + lists_bytes(cap, query_len * num_heads);
   if (ws_bytes < need)
     return mi_idx_fail(MI_IDX_ECAPACITY, "%s: ws_bytes %zu < %zu needed", who, ws_bytes, need);
   return MI_IDX_OK;
@@ -529,7 +530,6 @@ extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
   st = mi_idx_check_launch("score_topk_decode");
   if (st) return st;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(num_reqs), dim3(256), 0, s, seq_lens, num_reqs,
-                     query_len, num_heads, max_pages, (const int32_t *)plan,
-                     (const uint8_t *)workspace, topk_out);
+                     query_len, num_heads, max_pages, (const uint8_t *)workspace, topk_out);
   return mi_idx_check_launch("score_topk_decode (merge)");
 }

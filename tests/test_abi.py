@@ -50,7 +50,7 @@ def test_version_and_reason(m):
 
 def test_sizes(m):
     assert m.mi_idx_decode_plan_bytes(64) == 64 + (64 + 2048) * 16
-    assert m.mi_idx_decode_workspace_bytes(64, 1, 1) == 256 + (64 + 2048) * 16 * 8 + 8 * 64
+    assert m.mi_idx_decode_workspace_bytes(64, 1, 1) == 256 + 512 + (64 + 2048) * 16 * 8
     assert m.mi_idx_decode_workspace_bytes(0, 0, 1) == 0
     assert m.mi_idx_prefill_plan_bytes(8, 32768, 4) == 64 + (32768 // 64 + 8 + 1) * 16
     assert m.mi_idx_prefill_plan_bytes(1, 10, 9) == 0
