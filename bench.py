@@ -42,6 +42,12 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy three times (the reference "
                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    p.add_argument("--summarize-profiles", metavar="DIR",
+                   help="only turn the rocprofv3 CSV output under DIR (prof_trace, "
+                        "prof_fetch, prof_write, prof_copyf, prof_copyw, prof_sq) into "
+                        "profiles/<workload>_kernels.txt")
+    p.add_argument("--cpu-seconds", type=float, default=18.0,
+                   help="oracle time budget of the CPU baseline sample")
     return p.parse_args()
 
 
@@ -92,11 +98,12 @@ def measured_traffic(kernel, source):
     return None
 
 
-def cpu_baseline(w):
-    """The oracle on a bounded sample: two whole decode requests and 512 rows
-    of one prefill request, scoring + selection only (pages encoded before
-    the clock starts).  Extrapolated to the step by counts of requests and
-    rows."""
+def cpu_baseline(w, budget_s):
+    """The oracle on a bounded sample of the step: whole decode requests
+    (scoring + selection) until about a third of the time budget is spent,
+    then blocks of 256 rows of the first prefill request until the rest is;
+    pages are encoded before the clock starts.  Extrapolated to the step by
+    counts of requests and rows."""
     import oracle
     from threadpoolctl import threadpool_info
 
@@ -112,36 +119,41 @@ def cpu_baseline(w):
     sample_s = 0.0
     parts = []
     if w.Rd:
-        nreq = min(2, w.Rd)
-        t = 0.0
-        for r in range(nreq):
-            pages = request_pages(r)
+        t, nreq = 0.0, 0
+        dec_budget = budget_s / 3 if w.Rp else budget_s
+        while nreq < w.Rd and t < dec_budget:
+            pages = request_pages(nreq)
             t0 = time.perf_counter()
             bt = np.arange(pages.shape[0], dtype=np.int32)[None, :]
-            oracle.oracle_decode(w.q_codes[r * w.query_len:(r + 1) * w.query_len], pages, bt,
-                                 w.dec_seq_lens[r:r + 1], w.query_len)
+            oracle.oracle_decode(w.q_codes[nreq * w.query_len:(nreq + 1) * w.query_len], pages,
+                                 bt, w.dec_seq_lens[nreq:nreq + 1], w.query_len)
             t += time.perf_counter() - t0
+            nreq += 1
         sample_s += t
         est += t / nreq * w.Rd
-        parts.append(f"decode requests 0..{nreq - 1} ({w.query_len} rows x {w.H} heads each)")
+        parts.append(f"decode requests 0..{nreq - 1} of {w.Rd} ({w.query_len} rows x {w.H} "
+                     f"heads each)")
     if w.Rp:
         r = w.Rd
         pages = request_pages(r)
-        n = min(512, int(w.pre_new[0]))
-        rows = np.arange(n)
-        pos = int(w.pre_ctx[0]) + rows
-        hist = int(pos.max() // 128)
+        new = int(w.pre_new[0])
         T0 = w.n_decode_rows
+        pos_all = int(w.pre_ctx[0]) + np.arange(new)
         t0 = time.perf_counter()
-        kp = oracle.decode_pages(pages[:hist])
+        kp = oracle.decode_pages(pages[:int(pos_all.max() // 128)])
         t_pages = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        oracle.index_rows(oracle.e4m3fn_to_float(w.q_codes[T0:T0 + n]), pos, kp, 1.0)
-        t_rows = time.perf_counter() - t0
+        t_rows, n = 0.0, 0
+        while n < new and t_pages + t_rows < budget_s - sample_s:
+            m = min(256, new - n)
+            t0 = time.perf_counter()
+            oracle.index_rows(oracle.e4m3fn_to_float(w.q_codes[T0 + n:T0 + n + m]),
+                              pos_all[n:n + m], kp, 1.0)
+            t_rows += time.perf_counter() - t0
+            n += m
         sample_s += t_pages + t_rows
         est += w.Rp * t_pages + t_rows * (w.n_prefill_rows / n)
-        parts.append(f"prefill request {r}: page decode + {n} of {int(w.pre_new[0])} rows "
-                     f"x {w.H} heads over {hist} pages")
+        parts.append(f"prefill request {r}: page decode + rows 0..{n - 1} of {new} x {w.H} "
+                     f"heads over up to {int(pos_all[n - 1] // 128)} pages")
     return {"value": w.T / est if est > 0 else None, "unit": "query rows/s", "cores": int(cores),
             "kind": "oracle", "sample": "; ".join(parts) +
             f"; {sample_s:.1f} s of oracle time, extrapolated to the step by request and row "
@@ -159,6 +171,108 @@ def _cpu_model():
     return "unknown"
 
 
+KERNEL_SOURCES = {"decode_plan_kernel": "decode.hip", "decode_score_kernel": "decode.hip",
+                  "decode_merge_kernel": "decode.hip", "prefill_score_kernel": "prefill.hip",
+                  "insert_kernel": "insert.hip"}
+PROFILE_COMMANDS = [
+    ("kernel trace + stats", "rocprofv3 --kernel-trace --stats -T -f csv -d DIR/prof_trace -o trace"
+     " -- python bench.py --steps 5 --warmup 1 --no-cpu-baseline"),
+    ("FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_fetch -o fetch"
+     " -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
+    ("WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_write -o write"
+     " -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
+    ("copy calibration, FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_copyf -o copyf"
+     " -- python bench.py --copy-calibration"),
+    ("copy calibration, WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_copyw -o copyw"
+     " -- python bench.py --copy-calibration"),
+    ("SQ counters", "rocprofv3 --pmc SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS "
+     "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE -T -f csv "
+     "-d DIR/prof_sq -o sq -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
+    ("summary", "python bench.py --summarize-profiles DIR"),
+]
+
+
+def summarize_profiles(d, workload):
+    """Write profiles/<workload>_kernels.txt from the rocprofv3 CSVs under d."""
+    import collections
+    import csv
+    import hashlib
+
+    def counters(path):
+        out = collections.defaultdict(list)
+        for row in csv.DictReader(open(path)):
+            out[(row["Kernel_Name"], row["Counter_Name"])].append(float(row["Counter_Value"]))
+        return out
+
+    def per_kernel(cs, kernel, counter, part=False):
+        vals = [v for (k, c), v in cs.items()
+                if (kernel in k if part else k.startswith(kernel)) and c == counter]
+        return sum(vals[0]) / len(vals[0]) if vals else None
+
+    def sha(name):
+        path = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc", name)
+        return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+    stats = list(csv.DictReader(open(os.path.join(d, "prof_trace", "trace_kernel_stats.csv"))))
+    fetch = counters(os.path.join(d, "prof_fetch", "fetch_counter_collection.csv"))
+    write = counters(os.path.join(d, "prof_write", "write_counter_collection.csv"))
+    cf = counters(os.path.join(d, "prof_copyf", "copyf_counter_collection.csv"))
+    cw = counters(os.path.join(d, "prof_copyw", "copyw_counter_collection.csv"))
+    copy_f = per_kernel(cf, "copyBuffer", "FETCH_SIZE", part=True)
+    copy_w = per_kernel(cw, "copyBuffer", "WRITE_SIZE", part=True)
+    gib = float(1 << 30)
+    f_factor = gib / (copy_f * 1024)
+    w_factor = gib / (copy_w * 1024)
+    out = [f"# rocprofv3 summary: {workload} workload (bench.py defaults), one MI355X",
+           "#", "# commands (run from the repository root; DIR = the output folder):"]
+    for what, cmd in PROFILE_COMMANDS:
+        out.append(f"#   {what}: {cmd}")
+    out.append(f"# copy calibration: a plain 1 GiB device copy reads FETCH_SIZE {copy_f:.1f} KiB "
+               f"(factor {f_factor:.4f}) and WRITE_SIZE {copy_w:.1f} KiB (factor {w_factor:.4f}) "
+               "per launch")
+    out += ["", "## kernel stats (insert_kernel stages the pools outside the timed steps)",
+            "%-24s %6s %14s %14s %14s" % ("kernel", "calls", "avg_ns", "min_ns", "max_ns")]
+    for row in stats:
+        out.append("%-24s %6s %14.0f %14s %14s" % (row["Name"][:24], row["Calls"],
+                                                   float(row["AverageNs"]), row["MinNs"],
+                                                   row["MaxNs"]))
+    out += ["", "## HBM traffic per launch (counter KiB x 1024 x calibration factor)",
+            "%-24s %16s %16s %s" % ("kernel", "fetch_bytes", "write_bytes", "source_sha256[:16]")]
+    for k in ["decode_plan_kernel", "decode_score_kernel", "decode_merge_kernel",
+              "prefill_score_kernel"]:
+        fv, wv = per_kernel(fetch, k, "FETCH_SIZE"), per_kernel(write, k, "WRITE_SIZE")
+        if fv is None or wv is None:
+            continue
+        out.append("%-24s %16.0f %16.0f %s" % (k, fv * 1024 * f_factor, wv * 1024 * w_factor,
+                                               sha(KERNEL_SOURCES[k])))
+    sq_path = os.path.join(d, "prof_sq", "sq_counter_collection.csv")
+    if os.path.exists(sq_path):
+        sq = counters(sq_path)
+        out += ["", "## SQ counters per launch (GRBM_GUI_ACTIVE is summed over the 8 XCDs; "
+                "MFMA busy is summed over the 1024 SIMDs)"]
+        for k in ["prefill_score_kernel", "decode_score_kernel", "decode_merge_kernel"]:
+            g = per_kernel(sq, k, "GRBM_GUI_ACTIVE")
+            if g is None:
+                continue
+            vals = {c: per_kernel(sq, k, c) for c in
+                    ["SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS",
+                     "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES"]}
+            cyc = g / 8
+            line = f"{k}: cycles {cyc:.0f}"
+            for c, v in vals.items():
+                line += f" {c[3:]} {v:.0f}"
+            if vals["SQ_VALU_MFMA_BUSY_CYCLES"]:
+                line += "  mfma_util %.1f%%" % (100 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                                 (cyc * 1024))
+            if vals["SQ_INSTS_MFMA"]:
+                line += "  valu_per_mfma %.2f" % (vals["SQ_INSTS_VALU"] / vals["SQ_INSTS_MFMA"])
+            out.append(line)
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernels.txt")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    open(path, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -168,6 +282,9 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.summarize_profiles:
+        summarize_profiles(a.summarize_profiles, a.workload)
         return
     import torch
 
@@ -274,7 +391,7 @@ def main():
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -157,23 +157,6 @@ struct PendingTop {
   }
 };
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  lo = (uint32_t)__shfl_xor((int)lo, m, 64);
-  hi = (uint32_t)__shfl_xor((int)hi, m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Merge the lists held by lane l and lane l^m (disjoint id sets); afterwards
-// both lanes hold the best kHist of the union.
-__device__ __forceinline__ void merge_xor(TopList &t, int m) {
-  uint64_t other[kHist];
-#pragma unroll
-  for (int i = 0; i < kHist; ++i) other[i] = shfl_xor_u64(t.k[i], m);
-#pragma unroll
-  for (int i = 0; i < kHist; ++i) t.insert(other[i]);
-}
-
 // Workgroup barrier that orders LDS accesses only: global loads in flight
 // stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -15,7 +15,7 @@
 // reduces each page to its max over tokens, keeps a running top-15 per query
 // column in registers and writes the lists to the workspace.
 //
-// Merge (one workgroup per request, a second launch on the same stream, so
+// Merge (one wave per request column, a second launch on the same stream, so
 // the lists written by every XCD are visible without device-wide fences):
 // merges the request's item lists into the 16 output slots of every row.
 #include <cmath>
@@ -31,8 +31,6 @@ constexpr int kItemInts = 4;
 constexpr size_t kWsHeaderBytes = 256;
 constexpr int kListKeys = 16;         // 15 keys + an empty slot: 128-byte lists
 constexpr int kDepth = 3;             // pages in flight per wave (register ring)
-constexpr int kMergeKeys = 2048;      // LDS head keys of one merge pass
-constexpr int kCandKeys = 2048;       // LDS candidate keys of one merge pass
 constexpr int kMaxItemsPerReq = 256;  // bounds the merge's O(n^2) ranking
 
 // Plan header (int32): [0] item count, [1] chunk pages, [2] num_reqs,
@@ -53,72 +51,80 @@ __host__ __device__ inline size_t lists_offset(int num_reqs) {
   return kWsHeaderBytes + (((size_t)8 * num_reqs + 255) & ~(size_t)255);
 }
 
-__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t *__restrict__ seq_lens,
-                                                           int num_reqs, int max_pages,
-                                                           int query_len, int capacity, int rows,
-                                                           int32_t *__restrict__ plan,
-                                                           uint8_t *__restrict__ ws) {
-  __shared__ long long s_part[1024];
-  __shared__ int s_chunk;
-  const int tid = threadIdx.x;
-  const int nt = blockDim.x;
+constexpr int kPlanThreads = 256;
+
+__device__ __forceinline__ long long wave_sum(long long v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ long long wave_inclusive_scan(long long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long u = __shfl_up(v, off, 64);
+    v += lane >= off ? u : 0;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int history_of(const int32_t *seq_lens, int r, int max_pages) {
+  const int sl = seq_lens[r];
+  return min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
+    const int32_t *__restrict__ seq_lens, int num_reqs, int max_pages, int query_len,
+    int capacity, int rows, int32_t *__restrict__ plan, uint8_t *__restrict__ ws) {
+  constexpr int kWaves = kPlanThreads / 64;
+  __shared__ long long s_wave[2][kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int2 *req_info = reinterpret_cast<int2 *>(ws + kWsHeaderBytes);
   // Contiguous segment of requests per thread.
-  const int per = (num_reqs + nt - 1) / nt;
+  const int per = (num_reqs + kPlanThreads - 1) / kPlanThreads;
   const int r0 = min(num_reqs, tid * per), r1 = min(num_reqs, r0 + per);
   long long hsum = 0;
-  for (int r = r0; r < r1; ++r) {
-    const int sl = seq_lens[r];
-    hsum += min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
-  }
-  s_part[tid] = hsum;
+  for (int r = r0; r < r1; ++r) hsum += history_of(seq_lens, r, max_pages);
+  hsum = wave_sum(hsum);
+  if (lane == 0) s_wave[0][wave] = hsum;
   __syncthreads();
-  if (tid == 0) {
-    long long total = 0;
-    for (int i = 0; i < nt; ++i) total += s_part[i];
-    const long long c = (total + kTargetItems - 1) / kTargetItems;
-    s_chunk = (int)max((long long)kMinChunk, c);
-  }
-  __syncthreads();
-  const int chunk = s_chunk;
+  long long total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) total += s_wave[0][w];
+  const int chunk = (int)max((long long)kMinChunk, (total + kTargetItems - 1) / kTargetItems);
   auto chunk_of = [&](int h) {
     return max(chunk, (h + kMaxItemsPerReq - 1) / kMaxItemsPerReq);
   };
   // Item counts and their exclusive scan over the thread segments.
   long long cnt = 0;
   for (int r = r0; r < r1; ++r) {
-    const int sl = seq_lens[r];
-    const int h = min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
+    const int h = history_of(seq_lens, r, max_pages);
     const int c = chunk_of(h);
     cnt += max(1, (h + c - 1) / c);
   }
+  const long long incl = wave_inclusive_scan(cnt);
+  if (lane == 63) s_wave[1][wave] = incl;
   __syncthreads();
-  s_part[tid] = cnt;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial counts.
-  for (int off = 1; off < nt; off <<= 1) {
-    const long long v = tid >= off ? s_part[tid - off] : 0;
-    __syncthreads();
-    s_part[tid] += v;
-    __syncthreads();
+  long long first = incl - cnt, total_items = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    first += w < wave ? s_wave[1][w] : 0;
+    total_items += s_wave[1][w];
   }
-  long long first = s_part[tid] - cnt;
+  int4 *items = reinterpret_cast<int4 *>(plan + kPlanHeaderInts);
   for (int r = r0; r < r1; ++r) {
-    const int sl = seq_lens[r];
-    const int h = min(sl >= 1 ? (sl - 1) >> 7 : 0, max_pages);
+    const int h = history_of(seq_lens, r, max_pages);
     const int c = chunk_of(h);
     const int n = max(1, (h + c - 1) / c);
     for (int i = 0; i < n; ++i) {
       const long long it = first + i;
-      if (it < capacity)
-        reinterpret_cast<int4 *>(plan + kPlanHeaderInts)[it] =
-            make_int4(r, min(h, i * c), min(h, (i + 1) * c), 0);
+      if (it < capacity) items[it] = make_int4(r, min(h, i * c), min(h, (i + 1) * c), 0);
     }
     req_info[r] = make_int2((int)first, n);
     first += n;
   }
-  if (tid == nt - 1) {
-    const long long total_items = s_part[nt - 1];
+  if (tid == 0) {
     plan[0] = (int)min(total_items, (long long)capacity);
     plan[1] = chunk;
     plan[2] = num_reqs;
@@ -270,158 +276,159 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
   }
 }
 
-constexpr int kHead = 4;              // keys per list the merge reads up front
+constexpr int kHead = 4;                              // keys per list read up front
+constexpr int kMergeWaves = 4;                        // columns per merge workgroup
+constexpr int kListsPerLane = kMaxItemsPerReq / 64;   // a request's lists over 64 lanes
+constexpr int kFlatKeys = 256;                        // >= n * K for every n <= 256
+constexpr int kCandCap = 256;                         // > 15 lists x 15 keys
 
-struct MergeSmem {
-  uint64_t head[kMergeKeys];  // the lists' first kHead keys
-  uint64_t cand[kCandKeys];   // keys at or above a column's bound
-  uint64_t thr[64];
-  uint32_t ncand[64];
-  uint32_t over[64];
+struct __align__(16) MergeWaveSmem {   // 16-byte aligned pair reads
+  uint64_t flat[kFlatKeys + 2];   // top-K keys of every list (+ zero padding)
+  uint64_t cand[kCandCap + 2];    // keys at or above the bound (+ zero padding)
+  uint64_t thr;
+  uint32_t ncand;
 };
 
-// One workgroup per request: merge the request's n item lists, for every
-// column (row x head), into its 16 output slots.
+__device__ __forceinline__ uint64_t key_lo(const u32x4 &q) {
+  return ((uint64_t)q.y << 32) | q.x;
+}
+__device__ __forceinline__ uint64_t key_hi(const u32x4 &q) {
+  return ((uint64_t)q.w << 32) | q.z;
+}
+
+// Orders one wave's LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Number of keys in flat[0, n2) (n2 even, zero padded) greater than me.
+__device__ __forceinline__ int rank_in(const uint64_t *flat, int n2, uint64_t me) {
+  int rank = 0;
+#pragma unroll 4
+  for (int j = 0; j < n2; j += 2) {
+    const u32x4 q = *reinterpret_cast<const u32x4 *>(flat + j);
+    rank += (key_lo(q) > me ? 1 : 0) + (key_hi(q) > me ? 1 : 0);
+  }
+  return rank;
+}
+
+// One wave per column (row x head) of request blockIdx.x: merge the
+// request's n item lists (n <= 256, sorted, keys distinct across lists
+// because the items cover disjoint pages) into the 16 output slots.
 //
 // Any 15 distinct keys bound the 15th best key of the union from below; the
-// 15th largest of the lists' top-K keys (K = ceil(15 / n), so 1 once there
-// are 15 lists or more) is such a bound, and every key of the final top-15
-// is at or above it.  The keys at or above the bound are gathered and ranked
-// by counting (keys are distinct).  The first kHead keys of every list come
-// in with two 16-byte loads; deeper keys are read only from a list whose
-// kHead-th key still reaches the bound.  Columns go in batches that fit the
-// LDS arrays; a column whose candidates overflow its share is merged by
-// per-lane insertion and a butterfly instead (slower, same result).
-__global__ __launch_bounds__(256) void decode_merge_kernel(
+// 15th largest of the lists' top-K keys (K = ceil(15 / n), capped at 4, so 1
+// once there are 15 lists or more) is such a bound, and every key of the
+// final top-15 is at or above it.  Only lists whose first key reaches the
+// bound hold such keys, and there are at most 15 of them, so at most 225
+// candidates exist; they are gathered and ranked by counting.  When fewer
+// than 15 of the top-K keys are non-empty, every non-empty key is gathered
+// (at most 14 non-empty lists x 15).  Lane x holds lists x, x+64, ...: their
+// first four keys come in with two 16-byte loads, the rest only for a list
+// whose fourth key still reaches the bound.
+__global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
     const int32_t *__restrict__ seq_lens, int num_reqs, int query_len, int H, int max_pages,
     const uint8_t *__restrict__ ws, int32_t *__restrict__ out) {
-  __shared__ MergeSmem sm;
+  __shared__ MergeWaveSmem smem[kMergeWaves];
   const int r = blockIdx.x;
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int rows = query_len * H;
+  const int c = blockIdx.y * kMergeWaves + wave;
+  if (c >= rows) return;   // whole waves only; no workgroup barrier follows
+  MergeWaveSmem &sm = smem[wave];
+  const int qi = c / H, h = c - qi * H;
+  const int64_t T = (int64_t)r * query_len + qi;
+  const int p = seq_lens[r] - query_len + qi;
+  const int L = p >= 0 ? min(p >> 7, max_pages) : -1;
+  int32_t *dst = out + (T * H + h) * kTopk;
+  if (L < 0) {   // a padding row: every slot empty
+    if (lane < kTopk) dst[lane] = -1;
+    return;
+  }
   const uint64_t *lists = reinterpret_cast<const uint64_t *>(ws + lists_offset(num_reqs));
   const int2 info = reinterpret_cast<const int2 *>(ws + kWsHeaderBytes)[r];
-  const int first = info.x, n = info.y;
-  const int sl = seq_lens[r];
-  auto list_ptr = [&](int c, int x) -> const uint64_t * {
-    return lists + ((size_t)(first + x) * rows + c) * kListKeys;
+  const int first = info.x, n = max(1, min(info.y, kMaxItemsPerReq));
+  auto list_of = [&](int x) -> const u32x4 * {
+    return reinterpret_cast<const u32x4 *>(lists + ((size_t)(first + x) * rows + c) * kListKeys);
   };
-  auto emit = [&](int c, int slot, uint64_t v) {
-    const int qi = c / H, h = c - (c / H) * H;
-    const int64_t T = (int64_t)r * query_len + qi;
-    const int p = sl - query_len + qi;
-    const int L = p >= 0 ? min(p >> 7, max_pages) : -1;
-    out[(T * H + h) * kTopk + slot] = (L >= 0 && v != 0ull) ? key_id(v) : -1;
+  // 1. the first four keys of every list
+  u32x4 a[kListsPerLane], b[kListsPerLane];
+#pragma unroll
+  for (int j = 0; j < kListsPerLane; ++j) {
+    const u32x4 *src = list_of(min(lane + 64 * j, n - 1));
+    a[j] = src[0];
+    b[j] = src[1];
+  }
+  const int K = n >= kHist ? 1 : min(kHead, (kHist + n - 1) / n);
+  const int nK = n * K;
+#pragma unroll
+  for (int j = 0; j < kListsPerLane; ++j) {
+    const int x = lane + 64 * j;
+    if (x < n) {
+      uint64_t *f = sm.flat + x * K;
+      f[0] = key_lo(a[j]);
+      if (K > 1) f[1] = key_hi(a[j]);
+      if (K > 2) f[2] = key_lo(b[j]);
+      if (K > 3) f[3] = key_hi(b[j]);
+    }
+  }
+  if (lane == 0) {
+    sm.flat[nK] = 0ull;
+    sm.thr = 0ull;
+    sm.ncand = 0u;
+  }
+  wave_lds_sync();
+  // 2. the bound: the key of rank 14 among the top-K keys, if non-empty
+  const int nK2 = (nK + 1) & ~1;
+  for (int i = lane; i < nK; i += 64) {
+    const uint64_t me = sm.flat[i];
+    if (me != 0ull && rank_in(sm.flat, nK2, me) == kHist - 1) sm.thr = me;
+  }
+  wave_lds_sync();
+  const uint64_t thr = sm.thr ? sm.thr : 1ull;
+  // 3. gather every key at or above the bound
+  auto push = [&](uint64_t v) {
+    const uint32_t pos = atomicAdd(&sm.ncand, 1u);
+    if (pos < (uint32_t)kCandCap) sm.cand[pos] = v;
   };
-  const int K = n >= kHist ? 1 : min(kHead, (kHist + n - 1) / max(n, 1));
-  const int per_col = max(n * kHead, 1);
-  const int batch = max(1, min(rows, min(kMergeKeys / per_col, 64)));
-  for (int c0 = 0; c0 < rows; c0 += batch) {
-    const int nc = min(batch, rows - c0);
-    const int cand_cap = kCandKeys / nc;
-    // 1. the first kHead keys of every list
-    for (int p = tid; p < nc * n; p += nt) {
-      const int cl = p / n, x = p - cl * n;
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(list_ptr(c0 + cl, x));
-      const u32x4 a = src[0], b = src[1];
-      uint64_t *h = sm.head + (size_t)p * kHead;
-      h[0] = ((uint64_t)a.y << 32) | a.x;
-      h[1] = ((uint64_t)a.w << 32) | a.z;
-      h[2] = ((uint64_t)b.y << 32) | b.x;
-      h[3] = ((uint64_t)b.w << 32) | b.z;
-    }
-    for (int c = tid; c < nc; c += nt) {
-      sm.thr[c] = 0ull;
-      sm.ncand[c] = 0u;
-      sm.over[c] = 0u;
-    }
-    __syncthreads();
-    // 2. the bound: the 15th largest of the lists' top-K keys (none if
-    // there are fewer than 15 of them)
-    for (int p = tid; p < nc * n * K; p += nt) {
-      const int cl = p / (n * K), i = p - cl * (n * K);
-      const uint64_t *hc = sm.head + (size_t)cl * n * kHead;
-      const uint64_t me = hc[(i / K) * kHead + i % K];
-      if (me == 0ull) continue;
-      int rank = 0;
-      for (int x = 0; x < n; ++x)
-        for (int k = 0; k < K; ++k) rank += hc[x * kHead + k] > me ? 1 : 0;
-      if (rank == kHist - 1) sm.thr[cl] = me;
-    }
-    __syncthreads();
-    // 3. gather every key at or above the bound
-    for (int p = tid; p < nc * n; p += nt) {
-      const int cl = p / n, x = p - cl * n;
-      const uint64_t thr = sm.thr[cl] ? sm.thr[cl] : 1ull;
-      const uint64_t *h = sm.head + (size_t)p * kHead;
-      int k = 0;
-      for (; k < kHead; ++k) {
-        const uint64_t v = h[k];
-        if (v < thr) break;
-        const uint32_t pos = atomicAdd(&sm.ncand[cl], 1u);
-        if (pos < (uint32_t)cand_cap) sm.cand[cl * cand_cap + pos] = v;
-        else sm.over[cl] = 1u;
-      }
-      if (k == kHead) {
-        const uint64_t *src = list_ptr(c0 + cl, x);
-        for (; k < kHist; ++k) {
-          const uint64_t v = src[k];
-          if (v < thr) break;
-          const uint32_t pos = atomicAdd(&sm.ncand[cl], 1u);
-          if (pos < (uint32_t)cand_cap) sm.cand[cl * cand_cap + pos] = v;
-          else sm.over[cl] = 1u;
-        }
-      }
-    }
-    __syncthreads();
-    // 4. rank them; slots past the candidates are empty
-    for (int p = tid; p < nc * kHist; p += nt) {
-      const int cl = p / kHist, k = p - cl * kHist;
-      if (!sm.over[cl] && k >= (int)sm.ncand[cl]) emit(c0 + cl, k, 0ull);
-    }
-    for (int p = tid; p < nc * cand_cap; p += nt) {
-      const int cl = p / cand_cap, i = p - cl * cand_cap;
-      const int m = (int)sm.ncand[cl];
-      if (sm.over[cl] || i >= m) continue;
-      const uint64_t *cc = sm.cand + cl * cand_cap;
-      const uint64_t me = cc[i];
-      int rank = 0;
-      for (int b = 0; b < m; ++b) rank += cc[b] > me ? 1 : 0;
-      if (rank < kHist) emit(c0 + cl, rank, me);
-    }
-    // Overflowed columns: one wave, per-lane insertion, then a butterfly.
-    if (tid < 64) {
-      for (int cl = 0; cl < nc; ++cl) {
-        if (!sm.over[cl]) continue;
-        TopList acc;
-        acc.clear();
-        for (int x = tid; x < n; x += 64) {
-          const uint64_t *src = list_ptr(c0 + cl, x);
-          for (int k = 0; k < kHist; ++k) {
-            const uint64_t v = src[k];
-            if (v <= acc.threshold()) break;
-            acc.insert(v);
-          }
-        }
 #pragma unroll
-        for (int m = 1; m < 64; m <<= 1) merge_xor(acc, m);
-        if (tid < kHist) {
-          uint64_t v = 0ull;
+  for (int j = 0; j < kListsPerLane; ++j) {
+    const int x = lane + 64 * j;
+    bool live = x < n;
+    const uint64_t head[kHead] = {key_lo(a[j]), key_hi(a[j]), key_lo(b[j]), key_hi(b[j])};
 #pragma unroll
-          for (int k = 0; k < kHist; ++k) v = (k == tid) ? acc.k[k] : v;
-          emit(c0 + cl, tid, v);
-        }
+    for (int k = 0; k < kHead; ++k) {
+      live = live && head[k] >= thr;
+      if (live) push(head[k]);
+    }
+    if (live) {
+      const u32x4 *src = list_of(x) + 2;   // keys 4..15
+      u32x4 w[6];
+#pragma unroll
+      for (int i = 0; i < 6; ++i) w[i] = src[i];
+#pragma unroll
+      for (int k = 0; k < kHist - kHead; ++k) {
+        const uint64_t v = (k & 1) ? key_hi(w[k >> 1]) : key_lo(w[k >> 1]);
+        live = live && v >= thr;
+        if (live) push(v);
       }
     }
-    __syncthreads();
   }
-  // Slot 15: the local page (-1 for a padding row).
-  for (int c = tid; c < rows; c += nt) {
-    const int qi = c / H, h = c - (c / H) * H;
-    const int64_t T = (int64_t)r * query_len + qi;
-    const int p = sl - query_len + qi;
-    out[(T * H + h) * kTopk + kHist] = p >= 0 ? min(p >> 7, max_pages) : -1;
+  wave_lds_sync();
+  const int m = min((int)sm.ncand, kCandCap);
+  if (lane == 0) sm.cand[m] = 0ull;
+  wave_lds_sync();
+  // 4. rank the candidates; slots past them are empty; slot 15 is the local page
+  const int m2 = (m + 1) & ~1;
+  for (int i = lane; i < m; i += 64) {
+    const uint64_t me = sm.cand[i];
+    const int rank = rank_in(sm.cand, m2, me);
+    if (rank < kHist) dst[rank] = key_id(me);
   }
+  if (lane >= m && lane < kHist) dst[lane] = -1;
+  if (lane == kHist) dst[kHist] = L;
 }
 
 }  // namespace mi_idx
@@ -474,7 +481,7 @@ extern "C" int mi_idx_plan_decode(const int32_t *seq_lens, int num_reqs, int que
   if (((uintptr_t)plan % 16) || ((uintptr_t)workspace % 16))
     return mi_idx_fail(MI_IDX_EINVAL, "plan_decode: plan and workspace must be 16-byte aligned");
   const int cap = plan_capacity(plan_bytes);
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, seq_lens,
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, seq_lens,
                      num_reqs, max_pages, query_len, cap, query_len * num_heads, (int32_t *)plan,
                      (uint8_t *)workspace);
   return mi_idx_check_launch("plan_decode");
@@ -529,7 +536,9 @@ extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
 #undef MI_IDX_LAUNCH_DEC
   st = mi_idx_check_launch("score_topk_decode");
   if (st) return st;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_reqs), dim3(256), 0, s, seq_lens, num_reqs,
+  hipLaunchKernelGGL(decode_merge_kernel,
+                     dim3(num_reqs, (query_len * num_heads + kMergeWaves - 1) / kMergeWaves),
+                     dim3(64 * kMergeWaves), 0, s, seq_lens, num_reqs,
                      query_len, num_heads, max_pages, (const uint8_t *)workspace, topk_out);
   return mi_idx_check_launch("score_topk_decode (merge)");
 }
