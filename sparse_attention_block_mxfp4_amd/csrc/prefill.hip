@@ -24,6 +24,10 @@ constexpr int kXcds = 8;                // MI355X accelerator complex dies
 #define MI_IDX_PREFILL_CGW 4
 #endif
 constexpr int kPrefillCgw = MI_IDX_PREFILL_CGW;   // 16-column groups per wave
+#ifndef MI_IDX_PREFILL_STREAMS
+#define MI_IDX_PREFILL_STREAMS 2
+#endif
+constexpr int kPrefillStreams = MI_IDX_PREFILL_STREAMS;   // page streams per workgroup
 
 inline int rows_per_tile(int H) { return kTileCols / H; }
 
@@ -48,28 +52,35 @@ __device__ __forceinline__ int page_token(int tl, int t16) {
 #endif
 }
 
-// CGW = 16-column MFMA groups per wave; the workgroup has 16 / CGW waves
-// and always covers kTileCols = 256 query columns.
-template <int CGW, bool kScores>
-__global__ __launch_bounds__(64 * (16 / CGW)) void prefill_score_kernel(
+// CGW = 16-column MFMA groups per wave: 16 / CGW waves cover the tile's
+// kTileCols = 256 query columns.  NS page streams of such wave sets share the
+// workgroup: stream s walks pages s, s + NS, s + 2 NS, ... with LDS buffers of
+// its own, so a SIMD holds NS waves that interleave MFMA, VALU and waits.  At
+// the end the streams' lists are merged through LDS by stream 0.
+template <int CGW, int NS, bool kScores>
+__global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ pages, int64_t num_blocks,
     const int32_t *__restrict__ block_table, int64_t bt_stride,
     const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ context_lens, int num_reqs, int64_t total_q, int H,
     int max_pages, float scale, const int32_t *__restrict__ plan, int32_t *__restrict__ out,
     float *__restrict__ scores_out) {
-  constexpr int NW = 16 / CGW;                       // waves per workgroup
-  constexpr int NT = 64 * NW;                        // threads per workgroup
+  constexpr int NW = 16 / CGW;                       // waves per stream
+  constexpr int NT = 64 * NW;                        // threads per stream
   constexpr int kLoads = (kChunks + NT - 1) / NT;    // 16-byte chunks per thread
-  // Two LDS page buffers, each in the page's global byte layout (token t at
-  // 68*t).
-  __shared__ __attribute__((aligned(16))) uint8_t s_page[2][kPageBytes];
+  static_assert(NS >= 1 && NS <= 2, "one or two page streams");
+  static_assert(NS == 1 || kHist * NT * 8 <= NS * 2 * kPageBytes,
+                "the stream merge reuses the page buffers");
+  // Two LDS page buffers per stream, each in the page's global byte layout
+  // (token t at 68*t).
+  __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][2][kPageBytes];
 
   if ((int)blockIdx.x >= plan[0]) return;
   const int4 tile = reinterpret_cast<const int4 *>(plan + kPreHeaderInts)[blockIdx.x];
   const int r = tile.x, row0 = tile.y, nrows = tile.z;
   if (r < 0 || r >= num_reqs) return;
-  const int tid = threadIdx.x;
+  const int stream = NS == 1 ? 0 : (int)threadIdx.x / NT;
+  const int tid = (int)threadIdx.x - stream * NT;    // thread within its stream
   const int wave = tid >> 6, lane = tid & 63;
   const int t16 = lane & 15, g = lane >> 4;
   const int ctx = context_lens[r];
@@ -139,7 +150,7 @@ __global__ __launch_bounds__(64 * (16 / CGW)) void prefill_score_kernel(
     if (kLoads > 2) R2 = src[min(tid + 2 * NT, kChunks - 1)];
   };
   auto pf_commit = [&](int buf, const uint4 &R0, const uint4 &R1, const uint4 &R2) {
-    uint4 *d = reinterpret_cast<uint4 *>(s_page[buf]);
+    uint4 *d = reinterpret_cast<uint4 *>(s_page[stream][buf]);
     if (tid < kChunks) d[tid] = R0;
     if (kLoads > 1 && tid + NT < kChunks) d[tid + NT] = R1;
     if (kLoads > 2 && tid + 2 * NT < kChunks) d[tid + 2 * NT] = R2;
@@ -149,7 +160,7 @@ __global__ __launch_bounds__(64 * (16 / CGW)) void prefill_score_kernel(
   // tile tl-1's are folded into the maxima, then the reduction over the 4
   // lane groups (token quarters) with VALU lane swaps.  No branches.
   auto page_max = [&](int buf) -> float {
-    const uint8_t *pg = s_page[buf];
+    const uint8_t *pg = s_page[stream][buf];
     u32x4 A[8];
     uint32_t S[8];
 #pragma unroll
@@ -198,35 +209,54 @@ __global__ __launch_bounds__(64 * (16 / CGW)) void prefill_score_kernel(
     if (kScores && writer && ok) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
   };
 
-  if (J > 0) {
-    pf_issue(0, e0, e1, e2);
+  // Step k of the stream handles page NS * k + stream; a page index at or
+  // past J re-reads page J - 1 and is not taken (J >= every row's L).
+  const int K = (J + NS - 1) / NS;
+  auto pj = [&](int k) { return NS * k + stream; };
+  if (K > 0) {
+    pf_issue(pj(0), e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
-    pf_issue(1, o0, o1, o2);
+    pf_issue(pj(1), o0, o1, o2);
     __builtin_amdgcn_sched_barrier(0);
     pf_commit(0, e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
-    pf_issue(2, e0, e1, e2);
+    pf_issue(pj(2), e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
-    for (int j = 0; j < J; j += 2) {
-      // even page j in LDS buffer 0; pages j+1 (slot 1) and j+2 (slot 0) in flight
+    for (int k = 0; k < K; k += 2) {
+      // step k in LDS buffer 0; steps k+1 (slot 1) and k+2 (slot 0) in flight
       pf_commit(1, o0, o1, o2);
       __builtin_amdgcn_sched_barrier(0);
-      pf_issue(j + 3, o0, o1, o2);
+      pf_issue(pj(k + 3), o0, o1, o2);
       __builtin_amdgcn_sched_barrier(0);
-      take(page_max(0), j);
+      take(page_max(0), pj(k));
       lds_barrier();
-      // odd page j+1 in LDS buffer 1; pages j+2 (slot 0) and j+3 (slot 1) in flight
+      // step k+1 in LDS buffer 1; steps k+2 (slot 0) and k+3 (slot 1) in flight
       pf_commit(0, e0, e1, e2);
       __builtin_amdgcn_sched_barrier(0);
-      pf_issue(j + 4, e0, e1, e2);
+      pf_issue(pj(k + 4), e0, e1, e2);
       __builtin_amdgcn_sched_barrier(0);
-      take(page_max(1), j + 1);
+      take(page_max(1), pj(k + 1));
       lds_barrier();
     }
   }
   top.flush();
-  if (writer && my_rl < nrows && myT < total_q)
+  if constexpr (NS == 2) {
+    // Stream 1 hands its lists to stream 0 through the (now idle) page
+    // buffers: key i of thread t at [i * NT + t].  The streams saw disjoint
+    // pages, so inserting one list into the other gives the top-15 of both.
+    uint64_t *s_lists = reinterpret_cast<uint64_t *>(&s_page[0][0][0]);
+    if (stream == 1) {
+#pragma unroll
+      for (int i = 0; i < kHist; ++i) s_lists[i * NT + tid] = top.top.k[i];
+    }
+    lds_barrier();
+    if (stream == 0) {
+#pragma unroll
+      for (int i = 0; i < kHist; ++i) top.top.insert_nb(s_lists[i * NT + tid]);
+    }
+  }
+  if (stream == 0 && writer && my_rl < nrows && myT < total_q)
     write_row(out + (myT * H + my_h) * kTopk, top.top, myL);
 }
 
@@ -399,14 +429,14 @@ extern "C" int mi_idx_score_topk_prefill(const uint8_t *q, const uint8_t *pages,
   if ((size_t)kPreHeaderInts * 4 + (size_t)num_tiles * 16 > plan_bytes)
     return mi_idx_fail(MI_IDX_ECAPACITY, "score_topk_prefill: num_tiles %d exceeds plan_bytes",
                        num_tiles);
-  const dim3 grid(num_tiles), block(64 * (16 / kPrefillCgw));
+  const dim3 grid(num_tiles), block(64 * kPrefillStreams * (16 / kPrefillCgw));
   if (scores_out)
-    hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, true>), grid, block, 0,
+    hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, kPrefillStreams, true>), grid, block, 0,
                        (hipStream_t)stream, q, pages, num_blocks, block_table, bt_stride,
                        cu_seqlens_q, seq_lens, context_lens, num_reqs, total_q, num_heads,
                        max_pages, scale, (const int32_t *)plan, topk_out, scores_out);
   else
-    hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, false>), grid, block, 0,
+    hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, kPrefillStreams, false>), grid, block, 0,
                        (hipStream_t)stream, q, pages, num_blocks, block_table, bt_stride,
                        cu_seqlens_q, seq_lens, context_lens, num_reqs, total_q, num_heads,
                        max_pages, scale, (const int32_t *)plan, topk_out, scores_out);
