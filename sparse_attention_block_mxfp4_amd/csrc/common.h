@@ -146,14 +146,33 @@ struct PendingTop {
     p0 = p1 = p2 = p3 = 0ull;
     n = 0;
   }
-  __device__ __forceinline__ void push(uint64_t key) {
+  // Shift key into the buffer if it beats the list's 15th key (no branch).
+  __device__ __forceinline__ void push_only(uint64_t key) {
     const bool c = key > top.k[kHist - 1];
     p3 = c ? p2 : p3;
     p2 = c ? p1 : p2;
     p1 = c ? p0 : p1;
     p0 = c ? key : p0;
     n += c ? 1 : 0;
+  }
+  // As push_only, with an extra bound: keys at or below `floor` are dropped
+  // (a lower bound on the final 15th key known from elsewhere).
+  __device__ __forceinline__ void push_only(uint64_t key, uint64_t floor) {
+    const uint64_t t = top.k[kHist - 1] > floor ? top.k[kHist - 1] : floor;
+    const bool c = key > t;
+    p3 = c ? p2 : p3;
+    p2 = c ? p1 : p2;
+    p1 = c ? p0 : p1;
+    p0 = c ? key : p0;
+    n += c ? 1 : 0;
+  }
+  // Keep room for the next key: flush once any lane's buffer is full.
+  __device__ __forceinline__ void make_room() {
     if (__any(n == 4)) flush();
+  }
+  __device__ __forceinline__ void push(uint64_t key) {
+    push_only(key);
+    make_room();
   }
 };
 

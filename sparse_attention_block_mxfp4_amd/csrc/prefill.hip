@@ -74,12 +74,24 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   // Two LDS page buffers per stream, each in the page's global byte layout
   // (token t at 68*t).
   __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][2][kPageBytes];
+  // Each stream's current 15th key per column, double-buffered by step
+  // parity: step k writes slot k & 1 and reads the partner's slot written in
+  // step k-1 (a barrier apart).  Keys are distinct, so a key at or below the
+  // partner's 15th key has 15 better keys there and cannot be in the final
+  // top-15: the partner's bound filters this stream's pushes.
+  __shared__ uint64_t s_floor[NS == 2 ? 2 : 1][NS][NS == 2 ? 64 * (16 / CGW) : 1];
+  // Flush requests, double-buffered by step parity: a wave whose lanes may
+  // run out of pending slots at the next step posts a flag; at that step
+  // every wave of the workgroup flushes, so one slow step serves all waves
+  // (the step barrier would make the others wait anyway).
+  __shared__ uint32_t s_need[2][NS * (16 / CGW)];
 
   if ((int)blockIdx.x >= plan[0]) return;
   const int4 tile = reinterpret_cast<const int4 *>(plan + kPreHeaderInts)[blockIdx.x];
   const int r = tile.x, row0 = tile.y, nrows = tile.z;
   if (r < 0 || r >= num_reqs) return;
-  const int stream = NS == 1 ? 0 : (int)threadIdx.x / NT;
+  // wave-uniform (page indices derived from it stay scalar)
+  const int stream = NS == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT);
   const int tid = (int)threadIdx.x - stream * NT;    // thread within its stream
   const int wave = tid >> 6, lane = tid & 63;
   const int t16 = lane & 15, g = lane >> 4;
@@ -155,11 +167,10 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     if (kLoads > 1 && tid + NT < kChunks) d[tid + NT] = R1;
     if (kLoads > 2 && tid + 2 * NT < kChunks) d[tid + 2 * NT] = R2;
   };
-  // Page max of every column of the wave for the page in LDS buffer buf:
-  // 8 token tiles x CGW MFMAs, tile tl's MFMAs into one accumulator set while
-  // tile tl-1's are folded into the maxima, then the reduction over the 4
-  // lane groups (token quarters) with VALU lane swaps.  No branches.
-  auto page_max = [&](int buf) -> float {
+  // Partial page maxima of the page in LDS buffer buf: 8 token tiles x CGW
+  // MFMAs, tile tl's MFMAs into one accumulator set while tile tl-1's are
+  // folded into m[cg] (this lane's 4 tokens of every tile).  No branches.
+  auto page_fold = [&](int buf, float (&m)[CGW]) {
     const uint8_t *pg = s_page[stream][buf];
     u32x4 A[8];
     uint32_t S[8];
@@ -170,7 +181,6 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       A[tl] = u32x4{a4.x, a4.y, a4.z, a4.w};
       S[tl] = tp[64 + g];
     }
-    float m[CGW];
 #pragma unroll
     for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
     v4f cx[CGW], cy[CGW];
@@ -191,6 +201,10 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     }
 #pragma unroll
     for (int cg = 0; cg < CGW; ++cg) m[cg] = fold4(m[cg], cy[cg]);
+  };
+  // The reduction over the 4 lane groups (token quarters) with VALU lane
+  // swaps: afterwards the lane holds the page max of its own column.
+  auto page_reduce = [&](const float (&m)[CGW]) -> float {
     if constexpr (CGW == 4) {
       // reduce-scatter: lane group g ends with column group g's max
       const float k0 = max_split32(m[0], m[2]);   // groups 0,1: cg 0; groups 2,3: cg 2
@@ -202,18 +216,49 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       return max_xor16(max_xor32(m[0]));
     }
   };
-  auto take = [&](float v, int j) {
-    const int phys = bt[min(j, jlast)];
-    const bool ok = j < myL && phys >= 0 && (int64_t)phys < num_blocks;
-    top.push(ok ? make_key(v, j) : 0ull);
+  // Offer page j's max to the column's list (j < 0 or past the row's
+  // history: nothing).  Branch-free; the caller makes room afterwards.
+  const int wave_id = stream * NW + wave;
+  auto take = [&](float v, int j, int parity) {
+    bool flush_now = false;
+#pragma unroll
+    for (int w = 0; w < NS * NW; ++w) flush_now = flush_now || s_need[parity ^ 1][w] != 0u;
+    if (__builtin_amdgcn_readfirstlane(flush_now ? 1 : 0)) top.flush();   // same for every lane
+    const int phys = bt[max(0, min(j, jlast))];
+    const bool ok = j >= 0 && j < myL && phys >= 0 && (int64_t)phys < num_blocks;
+    if constexpr (NS == 2) {
+      const uint64_t floor = s_floor[parity ^ 1][stream ^ 1][tid];
+      top.push_only(ok ? make_key(v, j) : 0ull, floor);
+      s_floor[parity][stream][tid] = top.top.k[kHist - 1];
+    } else {
+      top.push_only(ok ? make_key(v, j) : 0ull);
+    }
     if (kScores && writer && ok) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
+    // After this push every lane holds at most 3 pending keys unless a flag
+    // is posted now (then all flush before the next push): 4 slots suffice.
+    const bool need = __any(top.n >= 3);
+    if (lane == 0) s_need[parity][wave_id] = need ? 1u : 0u;
   };
 
   // Step k of the stream handles page NS * k + stream; a page index at or
-  // past J re-reads page J - 1 and is not taken (J >= every row's L).
+  // past J re-reads page J - 1 and is not taken (J >= every row's L).  The
+  // walk is software-pipelined: step k's MFMAs share a basic block with the
+  // reduction and selection of step k-1, so that VALU work fills the MFMA
+  // pipeline's shadow.
   const int K = (J + NS - 1) / NS;
   auto pj = [&](int k) { return NS * k + stream; };
   if (K > 0) {
+    float ma[CGW], mb[CGW];
+#pragma unroll
+    for (int cg = 0; cg < CGW; ++cg) mb[cg] = -INFINITY;
+    if constexpr (NS == 2) {
+      s_floor[0][stream][tid] = 0ull;
+      s_floor[1][stream][tid] = 0ull;
+    }
+    if (lane == 0) {
+      s_need[0][wave_id] = 0u;
+      s_need[1][wave_id] = 0u;
+    }
     pf_issue(pj(0), e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
     pf_issue(pj(1), o0, o1, o2);
@@ -223,22 +268,22 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     pf_issue(pj(2), e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
-    for (int k = 0; k < K; k += 2) {
+    int k = 0;
+    for (; k < K; k += 2) {
       // step k in LDS buffer 0; steps k+1 (slot 1) and k+2 (slot 0) in flight
       pf_commit(1, o0, o1, o2);
-      __builtin_amdgcn_sched_barrier(0);
       pf_issue(pj(k + 3), o0, o1, o2);
-      __builtin_amdgcn_sched_barrier(0);
-      take(page_max(0), pj(k));
+      page_fold(0, ma);
+      take(page_reduce(mb), pj(k - 1), 0);
       lds_barrier();
       // step k+1 in LDS buffer 1; steps k+2 (slot 0) and k+3 (slot 1) in flight
       pf_commit(0, e0, e1, e2);
-      __builtin_amdgcn_sched_barrier(0);
       pf_issue(pj(k + 4), e0, e1, e2);
-      __builtin_amdgcn_sched_barrier(0);
-      take(page_max(1), pj(k + 1));
+      page_fold(1, mb);
+      take(page_reduce(ma), pj(k), 1);
       lds_barrier();
     }
+    take(page_reduce(mb), pj(k - 1), 0);
   }
   top.flush();
   if constexpr (NS == 2) {
