@@ -30,7 +30,7 @@ constexpr int kPlanHeaderInts = 16;
 constexpr int kItemInts = 4;
 constexpr size_t kWsHeaderBytes = 256;
 constexpr int kListKeys = 16;         // 15 keys + an empty slot: 128-byte lists
-constexpr int kDepth = 3;             // pages in flight per wave (register ring)
+constexpr int kDepth = 2;             // pages in flight per wave (register ring)
 constexpr int kMaxItemsPerReq = 256;  // bounds the merge's O(n^2) ranking
 
 // Plan header (int32): [0] item count, [1] chunk pages, [2] num_reqs,
