@@ -28,6 +28,7 @@ constexpr int kPrefillCgw = MI_IDX_PREFILL_CGW;   // 16-column groups per wave
 #define MI_IDX_PREFILL_STREAMS 2
 #endif
 constexpr int kPrefillStreams = MI_IDX_PREFILL_STREAMS;   // page streams per workgroup
+constexpr int kQueue = 16;              // per-column key queue (LDS)
 
 inline int rows_per_tile(int H) { return kTileCols / H; }
 
@@ -80,10 +81,13 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   // partner's 15th key has 15 better keys there and cannot be in the final
   // top-15: the partner's bound filters this stream's pushes.
   __shared__ uint64_t s_floor[NS == 2 ? 2 : 1][NS][NS == 2 ? 64 * (16 / CGW) : 1];
-  // Flush requests, double-buffered by step parity: a wave whose lanes may
-  // run out of pending slots at the next step posts a flag; at that step
-  // every wave of the workgroup flushes, so one slow step serves all waves
-  // (the step barrier would make the others wait anyway).
+  // Keys waiting to enter a column's list: a queue per thread, entry i of
+  // thread t at [i][t] (consecutive lanes, consecutive words).
+  __shared__ uint64_t s_queue[kQueue][NS * 64 * (16 / CGW)];
+  // Drain requests, double-buffered by step parity: a wave whose queues may
+  // fill up at the next step posts a flag; at that step every wave of the
+  // workgroup drains, so one slow step serves all waves (the step barrier
+  // would make the others wait anyway).
   __shared__ uint32_t s_need[2][NS * (16 / CGW)];
 
   if ((int)blockIdx.x >= plan[0]) return;
@@ -137,8 +141,15 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     J = plast >= 0 ? min(plast >> 7, max_pages) : 0;
     J = max(J, 0);
   }
-  PendingTop top;
+  // The column's top-15 (registers) and its queue (LDS): a key that beats
+  // the list's 15th key (and the partner stream's) is appended to the queue
+  // with no branch -- the write always happens, the count moves only for a
+  // qualifying key -- and queues are drained into the lists rarely, each
+  // wave running as many insertions as its fullest queue holds.
+  TopList top;
   top.clear();
+  int nq = 0;
+  const int qslot = stream * NT + tid;
 
   // Page pipeline.  Page p's 16-byte chunks are staged in register slot
   // p & 1 (kLoads chunks per thread), copied into LDS buffer p & 1, and
@@ -204,6 +215,13 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   };
   // The reduction over the 4 lane groups (token quarters) with VALU lane
   // swaps: afterwards the lane holds the page max of its own column.
+  // Keeps a step's MFMA chain inside the step: the empty asm consumes the
+  // folded maxima, so the compiler cannot sink the chain past the barrier
+  // into the next step (where it would stay live across a queue drain).
+  auto pin = [&](float (&m)[CGW]) {
+#pragma unroll
+    for (int cg = 0; cg < CGW; ++cg) asm volatile("" : "+v"(m[cg]));
+  };
   auto page_reduce = [&](const float (&m)[CGW]) -> float {
     if constexpr (CGW == 4) {
       // reduce-scatter: lane group g ends with column group g's max
@@ -219,24 +237,39 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   // Offer page j's max to the column's list (j < 0 or past the row's
   // history: nothing).  Branch-free; the caller makes room afterwards.
   const int wave_id = stream * NW + wave;
-  auto take = [&](float v, int j, int parity) {
-    bool flush_now = false;
+  auto drain = [&]() {
+#pragma unroll 1
+    for (int i = 0; i < kQueue; ++i) {
+      if (!__any(i < nq)) break;
+      const uint64_t v = s_queue[i][qslot];
+      top.insert_nb(i < nq ? v : 0ull);
+    }
+    nq = 0;
+  };
+  // At the start of a step (parity = the step's): drain every queue if any
+  // wave posted a flag in the previous step.
+  auto maybe_drain = [&](int parity) {
+    bool drain_now = false;
 #pragma unroll
-    for (int w = 0; w < NS * NW; ++w) flush_now = flush_now || s_need[parity ^ 1][w] != 0u;
-    if (__builtin_amdgcn_readfirstlane(flush_now ? 1 : 0)) top.flush();   // same for every lane
+    for (int w = 0; w < NS * NW; ++w) drain_now = drain_now || s_need[parity ^ 1][w] != 0u;
+    if (__builtin_amdgcn_readfirstlane(drain_now ? 1 : 0)) drain();   // same for every lane
+  };
+  auto take = [&](float v, int j, int parity) {
     const int phys = bt[max(0, min(j, jlast))];
     const bool ok = j >= 0 && j < myL && phys >= 0 && (int64_t)phys < num_blocks;
+    const uint64_t key = ok ? make_key(v, j) : 0ull;
+    uint64_t bound = top.k[kHist - 1];
     if constexpr (NS == 2) {
       const uint64_t floor = s_floor[parity ^ 1][stream ^ 1][tid];
-      top.push_only(ok ? make_key(v, j) : 0ull, floor);
-      s_floor[parity][stream][tid] = top.top.k[kHist - 1];
-    } else {
-      top.push_only(ok ? make_key(v, j) : 0ull);
+      bound = floor > bound ? floor : bound;
+      s_floor[parity][stream][tid] = top.k[kHist - 1];
     }
+    // Without a posted flag every queue holds at most kQueue - 3 keys here
+    // (a flag is posted at kQueue - 2), so the write stays inside the queue.
+    s_queue[nq][qslot] = key;
+    nq += key > bound ? 1 : 0;
     if (kScores && writer && ok) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
-    // After this push every lane holds at most 3 pending keys unless a flag
-    // is posted now (then all flush before the next push): 4 slots suffice.
-    const bool need = __any(top.n >= 3);
+    const bool need = __any(nq >= kQueue - 2);
     if (lane == 0) s_need[parity][wave_id] = need ? 1u : 0u;
   };
 
@@ -271,21 +304,26 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     int k = 0;
     for (; k < K; k += 2) {
       // step k in LDS buffer 0; steps k+1 (slot 1) and k+2 (slot 0) in flight
+      maybe_drain(0);
       pf_commit(1, o0, o1, o2);
       pf_issue(pj(k + 3), o0, o1, o2);
       page_fold(0, ma);
       take(page_reduce(mb), pj(k - 1), 0);
+      pin(ma);
       lds_barrier();
       // step k+1 in LDS buffer 1; steps k+2 (slot 0) and k+3 (slot 1) in flight
+      maybe_drain(1);
       pf_commit(0, e0, e1, e2);
       pf_issue(pj(k + 4), e0, e1, e2);
       page_fold(1, mb);
       take(page_reduce(ma), pj(k), 1);
+      pin(mb);
       lds_barrier();
     }
+    maybe_drain(0);
     take(page_reduce(mb), pj(k - 1), 0);
   }
-  top.flush();
+  drain();
   if constexpr (NS == 2) {
     // Stream 1 hands its lists to stream 0 through the (now idle) page
     // buffers: key i of thread t at [i * NT + t].  The streams saw disjoint
@@ -293,16 +331,16 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     uint64_t *s_lists = reinterpret_cast<uint64_t *>(&s_page[0][0][0]);
     if (stream == 1) {
 #pragma unroll
-      for (int i = 0; i < kHist; ++i) s_lists[i * NT + tid] = top.top.k[i];
+      for (int i = 0; i < kHist; ++i) s_lists[i * NT + tid] = top.k[i];
     }
     lds_barrier();
     if (stream == 0) {
 #pragma unroll
-      for (int i = 0; i < kHist; ++i) top.top.insert_nb(s_lists[i * NT + tid]);
+      for (int i = 0; i < kHist; ++i) top.insert_nb(s_lists[i * NT + tid]);
     }
   }
   if (stream == 0 && writer && my_rl < nrows && myT < total_q)
-    write_row(out + (myT * H + my_h) * kTopk, top.top, myL);
+    write_row(out + (myT * H + my_h) * kTopk, top, myL);
 }
 
 }  // namespace mi_idx
