@@ -52,13 +52,9 @@ __device__ __forceinline__ float fold4(float m, const v4f &c) {
 // equal scores prefer the lower id.  0 is "empty" (below every real key).
 __device__ __forceinline__ uint64_t make_key(float s, int id) {
   uint32_t u = __float_as_uint(s);
-  uint32_t ord;
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) {   // NaN (tested on the bits)
-    ord = 0u;
-  } else {
-    if (s == 0.0f) u = 0u;
-    ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
+  u = (u << 1) == 0u ? 0u : u;                                  // -0 -> +0
+  uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  ord = (u & 0x7FFFFFFFu) > 0x7F800000u ? 0u : ord;             // NaN lowest (bits)
   return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
 }
 

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
                 "the stream merge reuses the page buffers");
   // Two LDS page buffers per stream, each in the page's global byte layout
   // (token t at 68*t).
-  __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][2][kPageBytes];
+  // (+16 bytes: the landing slot of the threads that have no chunk to write)
+  __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][2][kPageBytes + 16];
   // Each stream's current 15th key per column, double-buffered by step
   // parity: step k writes slot k & 1 and reads the partner's slot written in
   // step k-1 (a barrier apart).  Keys are distinct, so a key at or below the
@@ -163,9 +164,16 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   static_assert(kLoads >= 1 && kLoads <= 3, "page staging takes 1..3 chunks per thread");
   // slot 0 (even pages): e0..e2, slot 1 (odd pages): o0..o2
   uint4 e0, e1, e2, o0, o1, o2;
-  auto pf_issue = [&](int jj, uint4 &R0, uint4 &R1, uint4 &R2) {
+  // Validity of the page of step s (bit s & 63), recorded when the page is
+  // issued; a step's page is taken 4 steps after its issue, long before the
+  // bit is reused 64 steps later.  Wave-uniform, so it lives in SGPRs.
+  uint64_t vmask = 0;
+  auto pf_issue = [&](int step, uint4 &R0, uint4 &R1, uint4 &R2) {
+    const int jj = NS * step + stream;
     const int phys = bt[min(jj, jlast)];
     const bool valid = phys >= 0 && (int64_t)phys < num_blocks;
+    const uint64_t bit = 1ull << (step & 63);
+    vmask = valid ? (vmask | bit) : (vmask & ~bit);
     const uint4 *src =
         reinterpret_cast<const uint4 *>(pages + (int64_t)(valid ? phys : 0) * kPageBytes);
     R0 = src[min(tid, kChunks - 1)];
@@ -173,10 +181,11 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     if (kLoads > 2) R2 = src[min(tid + 2 * NT, kChunks - 1)];
   };
   auto pf_commit = [&](int buf, const uint4 &R0, const uint4 &R1, const uint4 &R2) {
+    // No branches: a thread without a chunk writes the landing slot.
     uint4 *d = reinterpret_cast<uint4 *>(s_page[stream][buf]);
-    if (tid < kChunks) d[tid] = R0;
-    if (kLoads > 1 && tid + NT < kChunks) d[tid + NT] = R1;
-    if (kLoads > 2 && tid + 2 * NT < kChunks) d[tid + 2 * NT] = R2;
+    d[min(tid, kChunks)] = R0;
+    if (kLoads > 1) d[min(tid + NT, kChunks)] = R1;
+    if (kLoads > 2) d[min(tid + 2 * NT, kChunks)] = R2;
   };
   // Partial page maxima of the page in LDS buffer buf: 8 token tiles x CGW
   // MFMAs, tile tl's MFMAs into one accumulator set while tile tl-1's are
@@ -254,9 +263,9 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     for (int w = 0; w < NS * NW; ++w) drain_now = drain_now || s_need[parity ^ 1][w] != 0u;
     if (__builtin_amdgcn_readfirstlane(drain_now ? 1 : 0)) drain();   // same for every lane
   };
-  auto take = [&](float v, int j, int parity) {
-    const int phys = bt[max(0, min(j, jlast))];
-    const bool ok = j >= 0 && j < myL && phys >= 0 && (int64_t)phys < num_blocks;
+  auto take = [&](float v, int step, int parity) {
+    const int j = NS * step + stream;
+    const bool ok = (j >= 0) & (j < myL) & (((vmask >> (step & 63)) & 1ull) != 0ull);
     const uint64_t key = ok ? make_key(v, j) : 0ull;
     uint64_t bound = top.k[kHist - 1];
     if constexpr (NS == 2) {
@@ -275,11 +284,11 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
 
   // Step k of the stream handles page NS * k + stream; a page index at or
   // past J re-reads page J - 1 and is not taken (J >= every row's L).  The
-  // walk is software-pipelined: step k's MFMAs share a basic block with the
-  // reduction and selection of step k-1, so that VALU work fills the MFMA
-  // pipeline's shadow.
+  // walk is software-pipelined: step k runs the MFMAs of its page and the
+  // reduction and selection of step k-1's page.  The two streams do these
+  // in opposite orders, so the two waves that share a SIMD (one per stream)
+  // overlap one's MFMA chain with the other's selection work.
   const int K = (J + NS - 1) / NS;
-  auto pj = [&](int k) { return NS * k + stream; };
   if (K > 0) {
     float ma[CGW], mb[CGW];
 #pragma unroll
@@ -292,13 +301,13 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       s_need[0][wave_id] = 0u;
       s_need[1][wave_id] = 0u;
     }
-    pf_issue(pj(0), e0, e1, e2);
+    pf_issue(0, e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
-    pf_issue(pj(1), o0, o1, o2);
+    pf_issue(1, o0, o1, o2);
     __builtin_amdgcn_sched_barrier(0);
     pf_commit(0, e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
-    pf_issue(pj(2), e0, e1, e2);
+    pf_issue(2, e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     int k = 0;
@@ -306,22 +315,36 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       // step k in LDS buffer 0; steps k+1 (slot 1) and k+2 (slot 0) in flight
       maybe_drain(0);
       pf_commit(1, o0, o1, o2);
-      pf_issue(pj(k + 3), o0, o1, o2);
-      page_fold(0, ma);
-      take(page_reduce(mb), pj(k - 1), 0);
-      pin(ma);
+      pf_issue(k + 3, o0, o1, o2);
+      if (stream == 0) {
+        page_fold(0, ma);
+        pin(ma);
+        take(page_reduce(mb), k - 1, 0);
+      } else {
+        take(page_reduce(mb), k - 1, 0);
+        pin(mb);
+        page_fold(0, ma);
+        pin(ma);
+      }
       lds_barrier();
       // step k+1 in LDS buffer 1; steps k+2 (slot 0) and k+3 (slot 1) in flight
       maybe_drain(1);
       pf_commit(0, e0, e1, e2);
-      pf_issue(pj(k + 4), e0, e1, e2);
-      page_fold(1, mb);
-      take(page_reduce(ma), pj(k), 1);
-      pin(mb);
+      pf_issue(k + 4, e0, e1, e2);
+      if (stream == 0) {
+        page_fold(1, mb);
+        pin(mb);
+        take(page_reduce(ma), k, 1);
+      } else {
+        take(page_reduce(ma), k, 1);
+        pin(ma);
+        page_fold(1, mb);
+        pin(mb);
+      }
       lds_barrier();
     }
     maybe_drain(0);
-    take(page_reduce(mb), pj(k - 1), 0);
+    take(page_reduce(mb), k - 1, 0);
   }
   drain();
   if constexpr (NS == 2) {
