@@ -175,8 +175,9 @@ KERNEL_SOURCES = {"decode_plan_kernel": "decode.hip", "decode_score_kernel": "de
                   "decode_merge_kernel": "decode.hip", "prefill_score_kernel": "prefill.hip",
                   "insert_kernel": "insert.hip"}
 PROFILE_COMMANDS = [
-    ("kernel trace + stats", "rocprofv3 --kernel-trace --stats -T -f csv -d DIR/prof_trace -o trace"
-     " -- python bench.py --steps 5 --warmup 1 --no-cpu-baseline"),
+    ("kernel trace + stats (the bench's own timed configuration)",
+     "rocprofv3 --kernel-trace --stats -T -f csv -d DIR/prof_trace -o trace"
+     " -- python bench.py --no-cpu-baseline"),
     ("FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_fetch -o fetch"
      " -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
     ("WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_write -o write"
