@@ -3,10 +3,11 @@
 // A workgroup owns a tile of M consecutive query rows of one request and all
 // H heads: 256 query columns (column = row * H + head), 64 per wave, so each
 // wave holds four 16-column MFMA B operands in registers for the whole tile.
-// The tile walks its causal pages 0..L_max-1; each page (8704 bytes) is
-// staged once into LDS -- double-buffered, the next page's global loads in
-// flight while the current one is consumed -- and re-read by all four waves
-// as the MFMA A operand.  Rows never cross workgroups, so the top-15 of a
+// The tile walks its causal pages 0..L_max-1 in two interleaved page
+// streams of four waves each; each page (8704 bytes) is staged once into LDS
+// -- a ring of four buffers per stream, two pages per barrier, the next two
+// pages' global loads in flight while the current two are consumed -- and
+// re-read by the stream's four waves as the MFMA A operand.  Rows never cross workgroups, so the top-15 of a
 // column is final when the walk ends: no merge pass.
 #include <algorithm>
 #include <cmath>
@@ -29,6 +30,7 @@ constexpr int kPrefillCgw = MI_IDX_PREFILL_CGW;   // 16-column groups per wave
 #endif
 constexpr int kPrefillStreams = MI_IDX_PREFILL_STREAMS;   // page streams per workgroup
 constexpr int kQueue = 16;              // per-column key queue (LDS)
+constexpr int kBufs = 4;                // LDS page buffers per stream
 
 inline int rows_per_tile(int H) { return kTileCols / H; }
 
@@ -70,12 +72,12 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   constexpr int NT = 64 * NW;                        // threads per stream
   constexpr int kLoads = (kChunks + NT - 1) / NT;    // 16-byte chunks per thread
   static_assert(NS >= 1 && NS <= 2, "one or two page streams");
-  static_assert(NS == 1 || kHist * NT * 8 <= NS * 2 * kPageBytes,
+  static_assert(NS == 1 || kHist * NT * 8 <= NS * kBufs * kPageBytes,
                 "the stream merge reuses the page buffers");
   // Two LDS page buffers per stream, each in the page's global byte layout
   // (token t at 68*t).
   // (+16 bytes: the landing slot of the threads that have no chunk to write)
-  __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][2][kPageBytes + 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][kBufs][kPageBytes + 16];
   // Each stream's current 15th key per column, double-buffered by step
   // parity: step k writes slot k & 1 and reads the partner's slot written in
   // step k-1 (a barrier apart).  Keys are distinct, so a key at or below the
@@ -278,7 +280,12 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     s_queue[nq][qslot] = key;
     nq += key > bound ? 1 : 0;
     if (kScores && writer && ok) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
-    const bool need = __any(nq >= kQueue - 2);
+  };
+  // End of a block (two pushes per queue): without a posted flag every queue
+  // holds at most kQueue - 4 keys, so the next block's two writes stay
+  // inside the queue.
+  auto post = [&](int parity) {
+    const bool need = __any(nq >= kQueue - 3);
     if (lane == 0) s_need[parity][wave_id] = need ? 1u : 0u;
   };
 
@@ -306,42 +313,47 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     pf_issue(1, o0, o1, o2);
     __builtin_amdgcn_sched_barrier(0);
     pf_commit(0, e0, e1, e2);
+    pf_commit(1, o0, o1, o2);
     __builtin_amdgcn_sched_barrier(0);
     pf_issue(2, e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
+    pf_issue(3, o0, o1, o2);
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
-    int k = 0;
-    for (; k < K; k += 2) {
-      // step k in LDS buffer 0; steps k+1 (slot 1) and k+2 (slot 0) in flight
-      maybe_drain(0);
-      pf_commit(1, o0, o1, o2);
-      pf_issue(k + 3, o0, o1, o2);
-      if (stream == 0) {
-        page_fold(0, ma);
-        pin(ma);
-        take(page_reduce(mb), k - 1, 0);
-      } else {
-        take(page_reduce(mb), k - 1, 0);
-        pin(mb);
-        page_fold(0, ma);
-        pin(ma);
-      }
-      lds_barrier();
-      // step k+1 in LDS buffer 1; steps k+2 (slot 0) and k+3 (slot 1) in flight
-      maybe_drain(1);
-      pf_commit(0, e0, e1, e2);
+    // Blocks of two steps, one barrier each.  Block b reads steps 2b, 2b+1
+    // from buffers (2b) & 3, (2b+1) & 3, commits steps 2b+2, 2b+3 (loaded
+    // during block b-1) into the other two buffers, and issues the loads of
+    // steps 2b+4, 2b+5.  A buffer is rewritten one barrier after its reads.
+    auto block = [&](int k, int rb, int parity) {
+      maybe_drain(parity);
+      pf_commit(rb ^ 2, e0, e1, e2);
+      pf_commit((rb ^ 2) + 1, o0, o1, o2);
       pf_issue(k + 4, e0, e1, e2);
+      pf_issue(k + 5, o0, o1, o2);
       if (stream == 0) {
-        page_fold(1, mb);
-        pin(mb);
-        take(page_reduce(ma), k, 1);
-      } else {
-        take(page_reduce(ma), k, 1);
+        page_fold(rb, ma);
         pin(ma);
-        page_fold(1, mb);
+        take(page_reduce(mb), k - 1, parity);
+        page_fold(rb + 1, mb);
+        pin(mb);
+        take(page_reduce(ma), k, parity);
+      } else {
+        take(page_reduce(mb), k - 1, parity);
+        pin(mb);
+        page_fold(rb, ma);
+        pin(ma);
+        take(page_reduce(ma), k, parity);
+        pin(ma);
+        page_fold(rb + 1, mb);
         pin(mb);
       }
+      post(parity);
       lds_barrier();
+    };
+    int k = 0;
+    for (; k < K; k += 4) {
+      block(k, 0, 0);
+      block(k + 2, 2, 1);
     }
     maybe_drain(0);
     take(page_reduce(mb), k - 1, 0);
