@@ -7,8 +7,9 @@
 // streams of four waves each; each page (8704 bytes) is staged once into LDS
 // -- a ring of four buffers per stream, two pages per barrier, the next two
 // pages' global loads in flight while the current two are consumed -- and
-// re-read by the stream's four waves as the MFMA A operand.  Rows never cross workgroups, so the top-15 of a
-// column is final when the walk ends: no merge pass.
+// re-read by the stream's four waves as the MFMA A operand.  At the end the
+// two streams' lists are merged in LDS; rows never cross workgroups, so a
+// column's top-15 is final then: no merge pass.
 #include <algorithm>
 #include <cmath>
 #include <vector>
