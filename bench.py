@@ -33,8 +33,10 @@ METRIC = "index-K GB/s + query-rows/s (decode, prefill), % of HBM/MFMA peak, 1 G
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    # The GPU needs ~0.1 s of sustained work to reach its steady clocks; with
+    # only a few warmup steps the timed steps run ~10 % slow.
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="mixed_step")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--pool-copies", type=int, default=2)
