@@ -80,6 +80,11 @@ CONFIGS = {
     "edge_prefill": dict(prefill=dict(ctx=[0, 0, 127, 1, 1919, 5000],
                                       new=[1, 130, 2, 300, 257, 64]), H=3, budget=8),
     "edge_heads5": dict(decode=dict(R=5, lo=1, hi=7000, query_len=5), H=5),
+    # monotone-score cases (tests give them constructed K and Q; see
+    # tests/test_gpu_trends.py): long histories in which every page is, or
+    # no page after the first 15 is, a new top-15 entry
+    "trend_decode": dict(decode=dict(R=5, lo=20000, hi=30000, query_len=3), H=2),
+    "trend_prefill": dict(prefill=dict(R=2, new=200, ctx_lo=25000, ctx_hi=30000), H=4),
 }
 
 
