@@ -171,24 +171,33 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   // issued; a step's page is taken 4 steps after its issue, long before the
   // bit is reused 64 steps later.  Wave-uniform, so it lives in SGPRs.
   uint64_t vmask = 0;
+  // This thread's chunks of a page: byte offsets in global memory (the last
+  // chunk re-read by threads past it) and in an LDS buffer (the landing slot
+  // for those threads); loop-invariant.
+  const uint32_t goff0 = 16u * (uint32_t)min(tid, kChunks - 1);
+  const uint32_t goff1 = 16u * (uint32_t)min(tid + NT, kChunks - 1);
+  const uint32_t goff2 = 16u * (uint32_t)min(tid + 2 * NT, kChunks - 1);
+  const uint32_t loff0 = 16u * (uint32_t)min(tid, kChunks);
+  const uint32_t loff1 = 16u * (uint32_t)min(tid + NT, kChunks);
+  const uint32_t loff2 = 16u * (uint32_t)min(tid + 2 * NT, kChunks);
   auto pf_issue = [&](int step, uint4 &R0, uint4 &R1, uint4 &R2) {
     const int jj = NS * step + stream;
     const int phys = bt[min(jj, jlast)];
     const bool valid = phys >= 0 && (int64_t)phys < num_blocks;
     const uint64_t bit = 1ull << (step & 63);
     vmask = valid ? (vmask | bit) : (vmask & ~bit);
-    const uint4 *src =
-        reinterpret_cast<const uint4 *>(pages + (int64_t)(valid ? phys : 0) * kPageBytes);
-    R0 = src[min(tid, kChunks - 1)];
-    if (kLoads > 1) R1 = src[min(tid + NT, kChunks - 1)];
-    if (kLoads > 2) R2 = src[min(tid + 2 * NT, kChunks - 1)];
+    // wave-uniform page base + this thread's 32-bit chunk offsets
+    const uint8_t *base = pages + (int64_t)(valid ? phys : 0) * kPageBytes;
+    R0 = *reinterpret_cast<const uint4 *>(base + goff0);
+    if (kLoads > 1) R1 = *reinterpret_cast<const uint4 *>(base + goff1);
+    if (kLoads > 2) R2 = *reinterpret_cast<const uint4 *>(base + goff2);
   };
   auto pf_commit = [&](int buf, const uint4 &R0, const uint4 &R1, const uint4 &R2) {
     // No branches: a thread without a chunk writes the landing slot.
-    uint4 *d = reinterpret_cast<uint4 *>(s_page[stream][buf]);
-    d[min(tid, kChunks)] = R0;
-    if (kLoads > 1) d[min(tid + NT, kChunks)] = R1;
-    if (kLoads > 2) d[min(tid + 2 * NT, kChunks)] = R2;
+    uint8_t *d = s_page[stream][buf];
+    *reinterpret_cast<uint4 *>(d + loff0) = R0;
+    if (kLoads > 1) *reinterpret_cast<uint4 *>(d + loff1) = R1;
+    if (kLoads > 2) *reinterpret_cast<uint4 *>(d + loff2) = R2;
   };
   // Partial page maxima of the page in LDS buffer buf: 8 token tiles x CGW
   // MFMAs, tile tl's MFMAs into one accumulator set while tile tl-1's are
