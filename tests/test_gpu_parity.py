@@ -19,7 +19,8 @@ from workloads.device import DeviceWorkload
 pytestmark = pytest.mark.gpu
 
 SMALL = ["tiny_decode", "decode_batch_small", "multi_token_small", "ragged_prefill_small",
-         "mixed_small", "edge_short", "edge_wide", "edge_prefill", "edge_heads5"]
+         "mixed_small", "edge_short", "edge_wide", "edge_prefill", "edge_heads5",
+         "prefill_h1_small", "prefill_h8_small"]
 
 
 def _banner(msg):
@@ -163,6 +164,43 @@ def test_poisoned_block_table_tail_and_spare_pages_are_never_read():
     checker.compare(out, ref, scores, L)
     # error word of the decode workspace: no invalid page id, no overflow
     assert int(step.dec_ws[:4].view(torch.int32).item()) == 0
+
+
+def test_invalid_page_ids_inside_a_history_are_skipped():
+    """Block-table entries outside [0, num_blocks) inside a history are never
+    dereferenced: the page is skipped (as if its score were NaN, which the
+    oracle ranks last) and the decode workspace's error bit 0 is set.  Every
+    row here has at least 20 history pages, so a skipped page never has to
+    fill a slot."""
+    _banner("invalid page ids")
+    w = W.make_workload("mixed_small", 3)
+    m = lib()
+    dw = DeviceWorkload(w, m.mi_idx_insert_mxfp4)
+    ref, scores, L, _ = run_oracle(w)
+    bad_ids = {1: -3, 5: w.num_blocks + 7, 17: -(1 << 30)}
+    bt = dw.block_table.cpu().numpy()
+    for r in range(len(w.seq_lens)):
+        for j, v in bad_ids.items():
+            bt[r, j] = v
+    dw.block_table.copy_(torch.from_numpy(bt))
+    out, _, _, _, step = run_gpu(w, dw=dw)
+    # expected: the oracle's scores with the bad pages as NaN
+    scores_mod = []
+    ref_mod = np.array(ref)
+    for t in range(out.shape[0]):
+        assert int(L[t]) >= 20
+        row = []
+        for h in range(w.H):
+            s = np.array(scores[t][h], dtype=np.float64)
+            s[list(bad_ids)] = np.nan
+            row.append(s)
+            ref_mod[t, h] = oracle.select_row(s, int(L[t]))
+        scores_mod.append(row)
+    finite = [[np.where(np.isnan(s), -np.inf, s) for s in row] for row in scores_mod]
+    checker.compare(out, ref_mod, finite, L)
+    for t in range(out.shape[0]):
+        assert not set(bad_ids) & set(out[t, :, :15].ravel().tolist())
+    assert int(step.dec_ws[:4].view(torch.int32).item()) & 1 == 1
 
 
 def _full_size(name):
