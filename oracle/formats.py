@@ -49,6 +49,26 @@ def e4m3fn_to_float(codes):
     return np.where(s == 1, -mag, mag)
 
 
+def bf16_to_float(bits):
+    """bfloat16 bit pattern (uint16) -> float64 value.
+
+    sign s = bit 15, exponent e = bits 14..7 (bias 127), mantissa m = bits 6..0.
+    e == 0  : (-1)^s * (m/128) * 2^(1-127)    (subnormal)
+    e == 255: (-1)^s * inf if m == 0, else NaN
+    else    : (-1)^s * (1 + m/128) * 2^(e-127)
+    (The index-Q dtype the vllm "indexer_mxfp4" page accepts besides E4M3.)
+    """
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    s = (b >> 15) & 1
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    sub = (m / 128.0) * 2.0 ** (1 - 127)
+    nrm = (1.0 + m / 128.0) * np.exp2(e.astype(np.float64) - 127.0)
+    mag = np.where(e == 0, sub, nrm)
+    mag = np.where(e == 255, np.where(m == 0, np.inf, np.nan), mag)
+    return np.where(s == 1, -mag, mag)
+
+
 def e2m1_to_float(codes):
     """FP4 E2M1 nibble -> float64 value.
 

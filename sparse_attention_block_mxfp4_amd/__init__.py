@@ -36,12 +36,12 @@ _SIGS = {
     "mi_idx_decode_plan_bytes": (_sz, [_i32]),
     "mi_idx_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "mi_idx_plan_decode": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _sz, _vp]),
-    "mi_idx_score_topk_decode": (_i32, [_vp, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32, _i32,
-                                        _f32, _vp, _sz, _vp, _sz, _vp, _vp, _vp]),
+    "mi_idx_score_topk_decode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
+                                        _i32, _f32, _vp, _sz, _vp, _sz, _vp, _vp, _vp]),
     "mi_idx_prefill_plan_bytes": (_sz, [_i32, _i64, _i32]),
     "mi_idx_plan_prefill": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp, _vp, _vp]),
-    "mi_idx_score_topk_prefill": (_i32, [_vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i64,
-                                         _i32, _i32, _f32, _vp, _sz, _i32, _vp, _vp, _vp]),
+    "mi_idx_score_topk_prefill": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32,
+                                         _i64, _i32, _i32, _f32, _vp, _sz, _i32, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -95,6 +95,13 @@ def _need(t, name, dtypes, cuda=True, contiguous=True):
 
 _U8 = (torch.uint8,)
 _Q8 = (torch.uint8, torch.float8_e4m3fn)
+_QALL = _Q8 + (torch.bfloat16,)
+Q_E4M3, Q_BF16 = 0, 1
+
+
+def _q_dtype(q):
+    """The C ABI's index-Q dtype code of a query tensor."""
+    return Q_BF16 if q.dtype == torch.bfloat16 else Q_E4M3
 _I32 = (torch.int32,)
 
 
@@ -147,10 +154,10 @@ def mi_idx_plan_decode(seq_lens, query_len, num_heads, max_pages, plan, workspac
 
 def mi_idx_score_topk_decode(q, pages, block_table, seq_lens, query_len, max_pages, plan,
                              workspace, topk_out, scale=1.0, scores_out=None, stream=None):
-    """q [R*query_len, H, 128] E4M3 (uint8 or float8_e4m3fn); topk_out
-    [R*query_len, H, 16] int32; block_table [R, >=max_pages] int32 (row stride
-    taken from the tensor)."""
-    _need(q, "q", _Q8)
+    """q [R*query_len, H, 128] E4M3 (uint8 or float8_e4m3fn) or bfloat16;
+    topk_out [R*query_len, H, 16] int32; block_table [R, >=max_pages] int32
+    (row stride taken from the tensor)."""
+    _need(q, "q", _QALL)
     _need(pages, "pages", _U8)
     _need(block_table, "block_table", _I32, contiguous=False)
     if block_table.dim() != 2 or block_table.stride(1) != 1:
@@ -170,7 +177,7 @@ def mi_idx_score_topk_decode(q, pages, block_table, seq_lens, query_len, max_pag
         if tuple(scores_out.shape) != (R * query_len, H, max_pages):
             raise ValueError("scores_out must be [rows, H, max_pages]")
     st = lib.mi_idx_score_topk_decode(
-        _ptr(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
+        _ptr(q), _q_dtype(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
         block_table.stride(0), _ptr(seq_lens), R, query_len, H, max_pages, float(scale),
         _ptr(plan), plan.numel(), _ptr(workspace), workspace.numel(), _ptr(topk_out),
         _ptr(scores_out), _stream(stream))
@@ -209,9 +216,9 @@ def mi_idx_plan_prefill(cu_seqlens_q_host, seq_lens_host, num_heads, gather_budg
 def mi_idx_score_topk_prefill(q, pages, block_table, cu_seqlens_q, seq_lens, context_lens,
                               max_pages, plan, num_tiles, topk_out, scale=1.0, scores_out=None,
                               stream=None):
-    """q [total_q, H, 128] E4M3; topk_out [total_q, H, 16] int32 (may be a
-    row slice of a larger contiguous buffer)."""
-    _need(q, "q", _Q8)
+    """q [total_q, H, 128] E4M3 or bfloat16; topk_out [total_q, H, 16] int32
+    (may be a row slice of a larger contiguous buffer)."""
+    _need(q, "q", _QALL)
     _need(pages, "pages", _U8)
     _need(block_table, "block_table", _I32, contiguous=False)
     if block_table.dim() != 2 or block_table.stride(1) != 1:
@@ -233,7 +240,7 @@ def mi_idx_score_topk_prefill(q, pages, block_table, cu_seqlens_q, seq_lens, con
         if tuple(scores_out.shape) != (T, H, max_pages):
             raise ValueError("scores_out must be [total_q, H, max_pages]")
     st = lib.mi_idx_score_topk_prefill(
-        _ptr(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
+        _ptr(q), _q_dtype(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
         block_table.stride(0), _ptr(cu_seqlens_q), _ptr(seq_lens), _ptr(context_lens), R, T, H,
         max_pages, float(scale), _ptr(plan), plan.numel(), num_tiles, _ptr(topk_out),
         _ptr(scores_out), _stream(stream))

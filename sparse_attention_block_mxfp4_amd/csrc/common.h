@@ -38,6 +38,61 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4 &a, const v8i &b,
                                                           (int)a_scale, 0, 127);
 }
 
+// ---- bfloat16 index-Q ------------------------------------------------------
+// The block-scaled MFMA takes FP8/FP6/FP4 operands only, so a bf16 query runs
+// on the bf16 MFMA: the page's FP4 codes are converted to bf16 (exactly: an
+// E2M1 value times a power of two is a bf16 value) and a 16x16x128 tile
+// becomes four 16x16x32 steps.  A lane keeps its usual 16 code bytes (the 32
+// dims of one scale block); k-step s takes their dword s (8 dims), and the
+// query operand of k-step s holds the same 8 dims -- a permutation of the
+// summation order, which the dot product does not see.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// E8M0 byte -> the fp32 factor 2^(b-127) (b = 0: 2^-127, a subnormal;
+// b = 255: NaN).
+__device__ __forceinline__ float e8m0_scale(uint32_t b) {
+  b &= 0xFFu;
+  const uint32_t bits = b == 0u ? 0x00400000u : (b == 255u ? 0x7FC00000u : (b << 23));
+  return __uint_as_float(bits);
+}
+
+// Eight E2M1 codes (one dword, low nibble first) -> eight bf16 values times
+// the scale factor.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sf) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 3);
+  return bf16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// One 16x16x128 tile with a bf16 query: A as for mfma_fp4_fp8 (16 code bytes
+// and the E8M0 byte of the lane's 32-dim block); b[s] = the query's 8 bf16
+// values of dims 32*(l>>4) + 8s .. +8 for column (l & 15).  Same C layout.
+__device__ __forceinline__ v4f mfma_fp4_bf16(const u32x4 &a, const u32x4 (&b)[4],
+                                             uint32_t a_scale) {
+  const float sf = e8m0_scale(a_scale);
+  v4f c = {0.f, 0.f, 0.f, 0.f};
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16(a.x, sf),
+                                              __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16(a.y, sf),
+                                              __builtin_bit_cast(bf16x8, b[1]), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16(a.z, sf),
+                                              __builtin_bit_cast(bf16x8, b[2]), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp4x8_to_bf16(a.w, sf),
+                                              __builtin_bit_cast(bf16x8, b[3]), c, 0, 0, 0);
+  return c;
+}
+
+// Query operand of a bf16 column: qrow = the 128 bf16 values (256 bytes,
+// 16-byte aligned) of the column's (row, head).
+__device__ __forceinline__ void load_q_bf16(const uint8_t *qrow, int g, u32x4 (&b)[4]) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    b[s] = *reinterpret_cast<const u32x4 *>(qrow + 2 * (32 * g + 8 * s));
+}
+
 __device__ __forceinline__ float max4(const v4f &c) {
   return fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w));
 }

@@ -139,7 +139,9 @@ __device__ __forceinline__ uint64_t *item_list(uint64_t *lists, int item, int ro
   return lists + ((size_t)item * rows + col) * kListKeys;
 }
 
-template <int NCG, bool kScores>
+// kBf16: the query is bfloat16 (256 bytes per row and head) and the tiles run
+// on the bf16 MFMA (see mfma_fp4_bf16); otherwise E4M3 (128 bytes).
+template <int NCG, bool kScores, bool kBf16>
 __global__ __launch_bounds__(256) void decode_score_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ pages, int64_t num_blocks,
     const int32_t *__restrict__ block_table, int64_t bt_stride,
@@ -160,20 +162,29 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
 
   // Query fragments (B operand) and the causal bound of each column.
   v8i bq[NCG];
+  u32x4 bqh[kBf16 ? NCG : 1][4];
   int Lc[NCG];
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const int col = cg * 16 + t16;
     Lc[cg] = -1;
     bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bqh[cg][k] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (col < rows) {
       const int i = col / H, h = col - (col / H) * H;
       const int64_t T = (int64_t)r * query_len + i;
-      const uint8_t *qp = q + (T * H + h) * kDim;
-      const u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
-      const u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
-      bq[cg] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (kBf16) {
+        load_q_bf16(q + (T * H + h) * (2 * kDim), g, bqh[cg]);
+      } else {
+        const uint8_t *qp = q + (T * H + h) * kDim;
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
+        bq[cg] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
       const int p = sl - query_len + i;
       Lc[cg] = p >= 0 ? min(p >> 7, max_pages) : -1;
     }
@@ -235,7 +246,8 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
           for (int tile = 0; tile < 8; ++tile) {
 #pragma unroll
             for (int cg = 0; cg < NCG; ++cg)
-              m[cg] = fmaxf(m[cg], max4(mfma_fp4_fp8(a[u][tile], bq[cg], s[u][tile])));
+              m[cg] = fmaxf(m[cg], max4(kBf16 ? mfma_fp4_bf16(a[u][tile], bqh[kBf16 ? cg : 0], s[u][tile])
+                                              : mfma_fp4_fp8(a[u][tile], bq[cg], s[u][tile])));
           }
 #pragma unroll
           for (int cg = 0; cg < NCG; ++cg) {
@@ -487,7 +499,7 @@ extern "C" int mi_idx_plan_decode(const int32_t *seq_lens, int num_reqs, int que
   return mi_idx_check_launch("plan_decode");
 }
 
-extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
+extern "C" int mi_idx_score_topk_decode(const void *q, int q_dtype, const uint8_t *pages,
                                         int64_t num_blocks, const int32_t *block_table,
                                         int64_t bt_stride, const int32_t *seq_lens, int num_reqs,
                                         int query_len, int num_heads, int max_pages, float scale,
@@ -500,6 +512,9 @@ extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
   if (st) return st;
   if (!(scale > 0.0f) || !std::isfinite(scale))
     return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: scale must be positive and finite");
+  if (q_dtype != MI_IDX_Q_E4M3 && q_dtype != MI_IDX_Q_BF16)
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: q_dtype %d is neither E4M3 (0) nor "
+                                      "bf16 (1)", q_dtype);
   if (num_reqs == 0) return MI_IDX_OK;
   if (!q || !pages || !block_table || !seq_lens || !plan || !workspace || !topk_out)
     return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: null pointer");
@@ -516,17 +531,20 @@ extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
   const int ncg = (rows + 15) / 16;
   const dim3 grid((cap + 3) / 4), block(256);
   hipStream_t s = (hipStream_t)stream;
+  const uint8_t *qb = static_cast<const uint8_t *>(q);
+#define MI_IDX_LAUNCH_DEC1(N, SC, BF)                                                          \
+  hipLaunchKernelGGL((decode_score_kernel<N, SC, BF>), grid, block, 0, s, qb, pages,          \
+                     num_blocks, block_table, bt_stride, seq_lens, num_reqs, query_len,        \
+                     num_heads, max_pages, scale, (const int32_t *)plan, (uint8_t *)workspace, \
+                     scores_out)
 #define MI_IDX_LAUNCH_DEC(N)                                                                   \
-  if (scores_out)                                                                              \
-    hipLaunchKernelGGL((decode_score_kernel<N, true>), grid, block, 0, s, q, pages, num_blocks, \
-                       block_table, bt_stride, seq_lens, num_reqs, query_len, num_heads,       \
-                       max_pages, scale, (const int32_t *)plan, (uint8_t *)workspace,          \
-                       scores_out);                                                            \
-  else                                                                                         \
-    hipLaunchKernelGGL((decode_score_kernel<N, false>), grid, block, 0, s, q, pages,            \
-                       num_blocks, block_table, bt_stride, seq_lens, num_reqs, query_len,      \
-                       num_heads, max_pages, scale, (const int32_t *)plan,                     \
-                       (uint8_t *)workspace, scores_out)
+  if (q_dtype == MI_IDX_Q_BF16) {                                                              \
+    if (scores_out) MI_IDX_LAUNCH_DEC1(N, true, true);                                         \
+    else MI_IDX_LAUNCH_DEC1(N, false, true);                                                   \
+  } else {                                                                                     \
+    if (scores_out) MI_IDX_LAUNCH_DEC1(N, true, false);                                        \
+    else MI_IDX_LAUNCH_DEC1(N, false, false);                                                  \
+  }
   switch (ncg) {
     case 1: MI_IDX_LAUNCH_DEC(1); break;
     case 2: MI_IDX_LAUNCH_DEC(2); break;
@@ -534,6 +552,7 @@ extern "C" int mi_idx_score_topk_decode(const uint8_t *q, const uint8_t *pages,
     default: MI_IDX_LAUNCH_DEC(4); break;
   }
 #undef MI_IDX_LAUNCH_DEC
+#undef MI_IDX_LAUNCH_DEC1
   st = mi_idx_check_launch("score_topk_decode");
   if (st) return st;
   hipLaunchKernelGGL(decode_merge_kernel,

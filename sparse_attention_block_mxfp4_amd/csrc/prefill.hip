@@ -61,7 +61,9 @@ __device__ __forceinline__ int page_token(int tl, int t16) {
 // workgroup: stream s walks pages s, s + NS, s + 2 NS, ... with LDS buffers of
 // its own, so a SIMD holds NS waves that interleave MFMA, VALU and waits.  At
 // the end the streams' lists are merged through LDS by stream 0.
-template <int CGW, int NS, bool kScores>
+// kBf16: bfloat16 query (256 bytes per row and head) on the bf16 MFMA (see
+// mfma_fp4_bf16); otherwise E4M3.
+template <int CGW, int NS, bool kScores, bool kBf16>
 __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ pages, int64_t num_blocks,
     const int32_t *__restrict__ block_table, int64_t bt_stride,
@@ -108,23 +110,38 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   const int64_t q0 = cu_seqlens_q[r];
 
   // B operands: columns (wave*CGW + cg)*16 + t16.
-  v8i bq[CGW];
+  v8i bq[kBf16 ? 1 : CGW];
+  u32x4 bqh[kBf16 ? CGW : 1][4];
 #pragma unroll
   for (int cg = 0; cg < CGW; ++cg) {
     const int col = (wave * CGW + cg) * 16 + t16;
     const int rl = col / H, h = col - rl * H;
-    bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bqh[cg][k] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
     if (rl < nrows) {
       const int64_t T = q0 + row0 + rl;
       if (T < total_q) {
-        const uint8_t *qp = q + (T * H + h) * kDim;
-        const u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
-        const u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
-        bq[cg] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if constexpr (kBf16) {
+          load_q_bf16(q + (T * H + h) * (2 * kDim), g, bqh[cg]);
+        } else {
+          const uint8_t *qp = q + (T * H + h) * kDim;
+          const u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
+          const u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
+          bq[cg] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
       }
     }
   }
+  // One 16x16x128 tile of column group cg.
+  auto tile_mfma = [&](const u32x4 &a, int cg, uint32_t sc) -> v4f {
+    if constexpr (kBf16) return mfma_fp4_bf16(a, bqh[cg], sc);
+    else return mfma_fp4_fp8(a, bq[cg], sc);
+  };
   // The column this lane owns after the page-max reduction: with 4 groups
   // per wave each lane group owns one; with 2, lane groups g and g^1 both
   // hold group g>>1 (the even one writes it); with 1, all hold it.
@@ -204,6 +221,42 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   // folded into m[cg] (this lane's 4 tokens of every tile).  No branches.
   auto page_fold = [&](int buf, float (&m)[CGW]) {
     const uint8_t *pg = s_page[stream][buf];
+    if constexpr (kBf16) {
+      // bf16 query: each tile's codes are read and converted once (four
+      // bf16 k-steps), then every column group runs its four-MFMA chain;
+      // tile tl's chains go into one accumulator set while tile tl-1's are
+      // folded, as in the E4M3 path.
+#pragma unroll
+      for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
+      v4f cx[CGW], cy[CGW];
+#pragma unroll
+      for (int tl = 0; tl < 8; ++tl) {
+        const uint8_t *tp = pg + page_token(tl, t16) * kTokenBytes;
+        const uint32_t *a32 = reinterpret_cast<const uint32_t *>(tp + 16 * g);
+        const float sf = e8m0_scale(tp[64 + g]);
+        bf16x8 av[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) av[k] = fp4x8_to_bf16(a32[k], sf);
+#pragma unroll
+        for (int cg = 0; cg < CGW; ++cg) {
+          v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], __builtin_bit_cast(bf16x8, bqh[cg][k]),
+                                                        c, 0, 0, 0);
+          if (tl & 1) {
+            cy[cg] = c;
+            m[cg] = fold4(m[cg], cx[cg]);
+          } else {
+            cx[cg] = c;
+            if (tl > 0) m[cg] = fold4(m[cg], cy[cg]);
+          }
+        }
+      }
+#pragma unroll
+      for (int cg = 0; cg < CGW; ++cg) m[cg] = fold4(m[cg], cy[cg]);
+      return;
+    }
     u32x4 A[8];
     uint32_t S[8];
 #pragma unroll
@@ -217,16 +270,16 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
     v4f cx[CGW], cy[CGW];
 #pragma unroll
-    for (int cg = 0; cg < CGW; ++cg) cx[cg] = mfma_fp4_fp8(A[0], bq[cg], S[0]);
+    for (int cg = 0; cg < CGW; ++cg) cx[cg] = tile_mfma(A[0], cg, S[0]);
 #pragma unroll
     for (int tl = 1; tl < 8; ++tl) {
 #pragma unroll
       for (int cg = 0; cg < CGW; ++cg) {
         if (tl & 1) {
-          cy[cg] = mfma_fp4_fp8(A[tl], bq[cg], S[tl]);
+          cy[cg] = tile_mfma(A[tl], cg, S[tl]);
           m[cg] = fold4(m[cg], cx[cg]);
         } else {
-          cx[cg] = mfma_fp4_fp8(A[tl], bq[cg], S[tl]);
+          cx[cg] = tile_mfma(A[tl], cg, S[tl]);
           m[cg] = fold4(m[cg], cy[cg]);
         }
       }
@@ -527,7 +580,7 @@ extern "C" int mi_idx_plan_prefill(const int32_t *cu_seqlens_q_host, const int32
   return MI_IDX_OK;
 }
 
-extern "C" int mi_idx_score_topk_prefill(const uint8_t *q, const uint8_t *pages,
+extern "C" int mi_idx_score_topk_prefill(const void *q, int q_dtype, const uint8_t *pages,
                                          int64_t num_blocks, const int32_t *block_table,
                                          int64_t bt_stride, const int32_t *cu_seqlens_q,
                                          const int32_t *seq_lens, const int32_t *context_lens,
@@ -541,6 +594,9 @@ extern "C" int mi_idx_score_topk_prefill(const uint8_t *q, const uint8_t *pages,
                        num_heads);
   if (num_reqs < 0 || total_q < 0 || max_pages < 0 || num_tiles < 0)
     return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: negative size");
+  if (q_dtype != MI_IDX_Q_E4M3 && q_dtype != MI_IDX_Q_BF16)
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: q_dtype %d is neither E4M3 (0) nor "
+                                      "bf16 (1)", q_dtype);
   if (!(scale > 0.0f) || !std::isfinite(scale))
     return mi_idx_fail(MI_IDX_EINVAL, "score_topk_prefill: scale must be positive and finite");
   if (num_tiles == 0 || total_q == 0) return MI_IDX_OK;
@@ -558,15 +614,19 @@ extern "C" int mi_idx_score_topk_prefill(const uint8_t *q, const uint8_t *pages,
     return mi_idx_fail(MI_IDX_ECAPACITY, "score_topk_prefill: num_tiles %d exceeds plan_bytes",
                        num_tiles);
   const dim3 grid(num_tiles), block(64 * kPrefillStreams * (16 / kPrefillCgw));
-  if (scores_out)
-    hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, kPrefillStreams, true>), grid, block, 0,
-                       (hipStream_t)stream, q, pages, num_blocks, block_table, bt_stride,
-                       cu_seqlens_q, seq_lens, context_lens, num_reqs, total_q, num_heads,
-                       max_pages, scale, (const int32_t *)plan, topk_out, scores_out);
-  else
-    hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, kPrefillStreams, false>), grid, block, 0,
-                       (hipStream_t)stream, q, pages, num_blocks, block_table, bt_stride,
-                       cu_seqlens_q, seq_lens, context_lens, num_reqs, total_q, num_heads,
-                       max_pages, scale, (const int32_t *)plan, topk_out, scores_out);
+  const uint8_t *qb = static_cast<const uint8_t *>(q);
+#define MI_IDX_LAUNCH_PRE(SC, BF)                                                              \
+  hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, kPrefillStreams, SC, BF>), grid, block, \
+                     0, (hipStream_t)stream, qb, pages, num_blocks, block_table, bt_stride,    \
+                     cu_seqlens_q, seq_lens, context_lens, num_reqs, total_q, num_heads,       \
+                     max_pages, scale, (const int32_t *)plan, topk_out, scores_out)
+  if (q_dtype == MI_IDX_Q_BF16) {
+    if (scores_out) MI_IDX_LAUNCH_PRE(true, true);
+    else MI_IDX_LAUNCH_PRE(false, true);
+  } else {
+    if (scores_out) MI_IDX_LAUNCH_PRE(true, false);
+    else MI_IDX_LAUNCH_PRE(false, false);
+  }
+#undef MI_IDX_LAUNCH_PRE
   return mi_idx_check_launch("score_topk_prefill");
 }

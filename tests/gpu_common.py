@@ -54,11 +54,12 @@ def run_oracle(w, pool=None, scale=1.0):
     outs, scs, Ls = [], [], []
     if w.Rd:
         o, s, L = oracle.oracle_decode(w.q_codes[:w.n_decode_rows], pool, w.block_table[:w.Rd],
-                                       w.dec_seq_lens, w.query_len, scale)
+                                       w.dec_seq_lens, w.query_len, scale, q_dtype=w.q_dtype)
         outs.append(o), scs.extend(s), Ls.append(L)
     if w.Rp:
         o, s, L = oracle.oracle_prefill(w.q_codes[w.n_decode_rows:], pool, w.block_table[w.Rd:],
-                                        w.cu_seqlens_q, w.seq_lens[w.Rd:], w.pre_ctx, scale)
+                                        w.cu_seqlens_q, w.seq_lens[w.Rd:], w.pre_ctx, scale,
+                                        q_dtype=w.q_dtype)
         outs.append(o), scs.extend(s), Ls.append(L)
     return np.concatenate(outs), scs, np.concatenate(Ls), pool
 
@@ -79,7 +80,7 @@ def oracle_request_rows(w, r, rows_in_req, scale=1.0):
         p = r - w.Rd
         T0 = w.n_decode_rows + int(w.cu_seqlens_q[p])
         pos = int(w.pre_ctx[p]) + rows_in_req
-    q = oracle.e4m3fn_to_float(w.q_codes[T0 + rows_in_req])
+    q = oracle.q_values(w.q_codes[T0 + rows_in_req], w.q_dtype)
     hist = int(max(pos.max() // 128, 0)) if pos.max() >= 0 else 0
     kp = oracle.decode_pages(pages[:hist])
     out, sc, L = oracle.index_rows(q, pos, kp, scale)

@@ -102,9 +102,17 @@ class Exact:
             best = s if best is None or s > best else best
         return best
 
-    def run(self, q_codes, pool, block_table, req_of_row, pos_of_row, scale):
-        """Exact 16-slot output of every row: returns (out [T,H,16], scores)."""
+    def run(self, q_codes, pool, block_table, req_of_row, pos_of_row, scale, q_dtype="e4m3"):
+        """Exact 16-slot output of every row: returns (out [T,H,16], scores).
+        Index-Q values come from torch's own casts (E4M3 bytes or bfloat16
+        bit patterns)."""
         q_codes = np.asarray(q_codes)
+        if q_dtype == "bf16":
+            qv = torch.from_numpy(np.ascontiguousarray(q_codes.astype(np.uint16)).view(np.int16))
+            qv = qv.view(torch.bfloat16).double().numpy()
+            q_of = lambda row, h: [Fraction(float(v)) for v in qv[row, h]]
+        else:
+            q_of = lambda row, h: [self.e4m3[int(c)] for c in q_codes[row, h]]
         T, H, _ = q_codes.shape
         pool = np.asarray(pool, dtype=np.uint8).reshape(-1, 8704)
         out = np.full((T, H, 16), -1, dtype=np.int64)
@@ -117,7 +125,7 @@ class Exact:
             L = p // 128
             r = int(req_of_row[row])
             for h in range(H):
-                q = [self.e4m3[int(c)] for c in q_codes[row, h]]
+                q = q_of(row, h)
                 key = tuple(int(c) for c in q_codes[row, h])
                 s = []
                 for j in range(L):

@@ -68,12 +68,13 @@ def test_decode_argument_errors(m):
     P, W = plan.ctypes.data, ws.ctypes.data
     pb, wb = m.mi_idx_decode_plan_bytes(4), m.mi_idx_decode_workspace_bytes(4, 2, 2)
     buf = _fake().ctypes.data
-    ok = dict(q=buf, pages=buf, nb=10, bt=buf, bts=16, sl=buf, R=4, ql=2, H=2, mp=16, sc=1.0,
-              P=P, pb=pb, W=W, wb=wb, out=buf)
+    ok = dict(q=buf, qd=0, pages=buf, nb=10, bt=buf, bts=16, sl=buf, R=4, ql=2, H=2, mp=16,
+              sc=1.0, P=P, pb=pb, W=W, wb=wb, out=buf)
 
     def call(**kw):
         a = dict(ok, **kw)
-        return L.mi_idx_score_topk_decode(a["q"], a["pages"], a["nb"], a["bt"], a["bts"], a["sl"],
+        return L.mi_idx_score_topk_decode(a["q"], a["qd"], a["pages"], a["nb"], a["bt"], a["bts"],
+                                          a["sl"],
                                           a["R"], a["ql"], a["H"], a["mp"], a["sc"], a["P"],
                                           a["pb"], a["W"], a["wb"], a["out"], None, None)
     assert call(ql=9) == m.EUNSUPPORTED
@@ -89,6 +90,8 @@ def test_decode_argument_errors(m):
     assert call(bts=8) == m.EINVAL
     assert call(nb=0) == m.EINVAL
     assert call(q=buf + 4) == m.EINVAL          # misaligned
+    assert call(qd=2) == m.EINVAL               # neither E4M3 nor bf16
+    assert call(qd=-1) == m.EINVAL
     assert b"scale" in L.mi_idx_last_error() or True
     assert call(R=0) == m.OK                    # nothing to do, nothing launched
     assert L.mi_idx_plan_decode(buf, 4, 9, 2, 16, P, pb, W, wb, None) == m.EUNSUPPORTED
@@ -116,19 +119,21 @@ def test_prefill_argument_errors(m):
     L = m.lib
     buf = _fake().ctypes.data
     pb = m.mi_idx_prefill_plan_bytes(2, 100, 1)
-    args = [buf, buf, 10, buf, 16, buf, buf, buf, 2, 100, 1, 16, 1.0, buf, pb, 2, buf, None, None]
+    args = [buf, 0, buf, 10, buf, 16, buf, buf, buf, 2, 100, 1, 16, 1.0, buf, pb, 2, buf, None,
+            None]
 
     def call(i=None, v=None):
         a = list(args)
         if i is not None:
             a[i] = v
         return L.mi_idx_score_topk_prefill(*a)
-    assert call(10, 9) == m.EUNSUPPORTED
-    assert call(12, -1.0) == m.EINVAL
+    assert call(11, 9) == m.EUNSUPPORTED
+    assert call(13, -1.0) == m.EINVAL
     assert call(0, None) == m.EINVAL
-    assert call(15, 10 ** 6) == m.ECAPACITY
-    assert call(4, 8) == m.EINVAL
-    assert call(15, 0) == m.OK
+    assert call(16, 10 ** 6) == m.ECAPACITY
+    assert call(5, 8) == m.EINVAL
+    assert call(1, 5) == m.EINVAL               # unknown q dtype
+    assert call(16, 0) == m.OK
     cu = np.array([0, 5, 3], dtype=np.int32)
     sl = np.array([10, 10], dtype=np.int32)
     tiles, ch = ctypes.c_int(), ctypes.c_int()

@@ -38,6 +38,27 @@ def test_e8m0_all_codes_match_torch_cast():
     assert mine[127] == 1.0 and mine[0] == 2.0 ** -127 and mine[254] == 2.0 ** 127
 
 
+def test_bf16_all_patterns_match_torch_cast():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ours = F.bf16_to_float(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    assert np.array_equal(np.signbit(ours[ok]), np.signbit(ref[ok]))
+
+
+def test_bf16_golden_points():
+    # hand-derived from the format: sign | 8-bit exponent (bias 127) | 7-bit mantissa
+    pts = {0x3F80: 1.0, 0xC000: -2.0, 0x3FC0: 1.5, 0x0080: 2.0 ** -126,
+           0x0001: 2.0 ** -133, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,
+           0x7F80: np.inf, 0xFF80: -np.inf, 0x8000: -0.0, 0x4049: 3.140625}
+    for b, v in pts.items():
+        got = float(F.bf16_to_float(np.array([b], dtype=np.uint16))[0])
+        assert got == v and np.signbit(got) == np.signbit(v), (hex(b), got, v)
+    assert np.isnan(F.bf16_to_float(np.array([0x7FC0], dtype=np.uint16))[0])
+
+
 def test_e2m1_matches_hand_typed_table():
     g = pins.golden_e2m1()
     got = oracle.e2m1_to_float(np.arange(16))

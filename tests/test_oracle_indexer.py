@@ -6,6 +6,7 @@ queries, zero queries, identical pages) and invariants of the method.
 """
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -74,6 +75,26 @@ def test_exact_bruteforce_decode():
     req = [r for r in range(len(seq_lens)) for _ in range(ql)]
     pos = [p for s in seq_lens for p in range(int(s) - ql, int(s))]
     ex_out, ex_sc = pins.Exact().run(q, pool, bt, req, pos, scale)
+    assert np.array_equal(out, ex_out)
+    for (row, h), s in ex_sc.items():
+        assert scores[row][h].tolist() == [float(x) for x in s]
+    pins.check_invariants(out, L)
+
+
+def test_exact_bruteforce_decode_bf16_queries():
+    """bfloat16 index-Q (the other dtype of the vllm "indexer_mxfp4" page's
+    scorers): the oracle against exact rationals from torch's bf16 cast."""
+    rng = np.random.default_rng(11)
+    pool = _random_case(rng, 5)
+    seq_lens = np.array([2 * 128 + 9, 4 * 128 + 1], dtype=np.int32)
+    ql, H = 2, 2
+    bt = np.array([[3, 0, 4, 4, 4], [1, 2, 0, 3, 4]], dtype=np.int32)
+    qf = rng.standard_normal((len(seq_lens) * ql, H, 128)).astype(np.float32) * 3.0
+    q = torch.from_numpy(qf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    out, scores, L = oracle.oracle_decode(q, pool, bt, seq_lens, ql, 0.5, q_dtype="bf16")
+    req = [r for r in range(len(seq_lens)) for _ in range(ql)]
+    pos = [p for s in seq_lens for p in range(int(s) - ql, int(s))]
+    ex_out, ex_sc = pins.Exact().run(q, pool, bt, req, pos, 0.5, q_dtype="bf16")
     assert np.array_equal(out, ex_out)
     for (row, h), s in ex_sc.items():
         assert scores[row][h].tolist() == [float(x) for x in s]

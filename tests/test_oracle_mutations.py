@@ -15,6 +15,9 @@ from tests import test_oracle_plan as TP
 
 PINS = [
     TF.test_e4m3_all_codes_match_torch_cast,
+    TF.test_bf16_all_patterns_match_torch_cast,
+    TF.test_bf16_golden_points,
+    TI.test_exact_bruteforce_decode_bf16_queries,
     TF.test_e4m3_golden_points,
     TF.test_e2m1_matches_hand_typed_table,
     TF.test_encoder_matches_round_half_even_reference,
@@ -72,6 +75,13 @@ _orig_e4m3 = F.e4m3fn_to_float
 
 def _e4m3_bias8(codes):
     return _orig_e4m3(codes) / 2.0
+
+
+_orig_bf16 = F.bf16_to_float
+
+
+def _bf16_bias_126(bits):
+    return _orig_bf16(bits) * 2.0
 
 
 _orig_select = I.select_row
@@ -162,6 +172,8 @@ MUTATIONS = {
     "tokens_dims_transposed": [(I, "decode_pages", _decode_pages_transposed)],
     "e4m3_bias_8": [(F, "e4m3fn_to_float", _e4m3_bias8), (oracle, "e4m3fn_to_float", _e4m3_bias8),
                     (I, "e4m3fn_to_float", _e4m3_bias8)],
+    "bf16_bias_126": [(F, "bf16_to_float", _bf16_bias_126), (oracle, "bf16_to_float", _bf16_bias_126),
+                      (I, "bf16_to_float", _bf16_bias_126)],
     "ties_to_higher_id": [(I, "select_row", _select_ties_high), (oracle, "select_row", _select_ties_high)],
     "nan_ranks_first": [(I, "select_row", _select_nan_first), (oracle, "select_row", _select_nan_first)],
     "local_leaks": [(I, "select_row", _select_local_in_history)],

@@ -111,7 +111,8 @@ class Workload:
     num_blocks: int = 0
     width: int = 0
     block_table: np.ndarray = field(default=None)   # [R, width] int32
-    q_codes: np.ndarray = field(default=None)       # [T, H, 128] uint8
+    q_codes: np.ndarray = field(default=None)       # [T, H, 128] uint8 (E4M3) or uint16 (bf16)
+    q_dtype: str = "e4m3"
 
     @property
     def Rd(self):
@@ -161,9 +162,12 @@ class Workload:
         n_pl = max(1, int(round(self.planted * hist)))
         pages = rng.choice(hist, size=n_pl, replace=False)
         toks = rng.integers(0, PAGE_TOKENS, size=n_pl)
-        rows = self.q_codes[r * self.query_len:(r + 1) * self.query_len]
-        qv = torch.from_numpy(np.ascontiguousarray(rows)).view(
-            torch.float8_e4m3fn).float().numpy().reshape(-1, HEAD_DIM)
+        rows = np.ascontiguousarray(self.q_codes[r * self.query_len:(r + 1) * self.query_len])
+        if self.q_dtype == "bf16":
+            qv = torch.from_numpy(rows.view(np.int16)).view(torch.bfloat16).float().numpy()
+        else:
+            qv = torch.from_numpy(rows).view(torch.float8_e4m3fn).float().numpy()
+        qv = qv.reshape(-1, HEAD_DIM)
         norms = np.linalg.norm(qv, axis=1, keepdims=True)
         unit = qv / np.where(norms > 0, norms, 1.0)
         direction = 3.0 * np.sign(unit.sum(axis=0))
@@ -192,7 +196,10 @@ class Workload:
         return np.tile(poison_page(), (self.num_blocks, 1))
 
 
-def make_workload(name, seed=0, **overrides):
+def make_workload(name, seed=0, q_dtype="e4m3", **overrides):
+    """The named workload; ``q_dtype`` "e4m3" (bytes) or "bf16" (bfloat16 bit
+    patterns as uint16) for the index-Q, cast by torch from the same fp32
+    draw either way."""
     cfg = dict(CONFIGS[name])
     cfg.update(overrides)
     rng = np.random.default_rng([seed, 0])
@@ -238,7 +245,13 @@ def make_workload(name, seed=0, **overrides):
         w.block_table[r, :n] = w.phys[w.page_off[r]:w.page_off[r] + n]
     import torch
     qf = np.random.default_rng([seed, 2]).standard_normal((w.T, H, HEAD_DIM), dtype=np.float32)
-    w.q_codes = torch.from_numpy(qf).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    if q_dtype == "e4m3":
+        w.q_codes = torch.from_numpy(qf).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    elif q_dtype == "bf16":
+        w.q_codes = torch.from_numpy(qf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    else:
+        raise ValueError(f"unknown index-Q dtype {q_dtype!r}")
+    w.q_dtype = q_dtype
     return w
 
 

@@ -41,7 +41,11 @@ class DeviceWorkload:
                     for pool in self.pools:
                         insert_fn(kd, sd, pool)
                     del kd, sd
-        self.q = torch.from_numpy(np.ascontiguousarray(w.q_codes)).to(dev)
+        if w.q_dtype == "bf16":
+            self.q = torch.from_numpy(np.ascontiguousarray(w.q_codes).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        else:
+            self.q = torch.from_numpy(np.ascontiguousarray(w.q_codes)).to(dev)
         self.block_table = torch.from_numpy(w.block_table).to(dev)
         self.seq_lens = torch.from_numpy(w.seq_lens).to(dev)
         self.Rd = w.Rd
