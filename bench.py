@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_FP8_TFLOPS = 5000.0        # dense FP8 MFMA (the FP8 x FP4 scaled MFMA runs at this rate)
+PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA (the path of a bf16 index-Q)
 METRIC = "index-K GB/s + query-rows/s (decode, prefill), % of HBM/MFMA peak, 1 GPU"
 
 
@@ -40,6 +41,9 @@ def parse():
     p.add_argument("--workload", default="mixed_step")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--pool-copies", type=int, default=2)
+    p.add_argument("--q-dtype", choices=["e4m3", "bf16"], default="e4m3",
+                   help="index-Q dtype (E4M3 is the configured workload; bf16 runs the "
+                        "bf16-MFMA path)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy three times (the reference "
@@ -71,14 +75,15 @@ def algorithmic(w):
     history page)."""
     dec_hist = np.maximum((w.dec_seq_lens.astype(np.int64) - 1) // 128, 0)
     nd = w.n_decode_rows
-    dec_bytes = int(dec_hist.sum()) * (8704 + 4) + nd * w.H * (128 + 64)
+    qb = 256 if w.q_dtype == "bf16" else 128
+    dec_bytes = int(dec_hist.sum()) * (8704 + 4) + nd * w.H * (qb + 64)
     dec_pages = int(dec_hist.sum())
     cu = w.cu_seqlens_q
     pre_L = np.concatenate([(int(w.pre_ctx[r]) + np.arange(int(w.pre_new[r]))) // 128
                             for r in range(w.Rp)]) if w.Rp else np.zeros(0, dtype=np.int64)
     pre_flops = int(pre_L.sum()) * w.H * 2 * 128 * 128
     pre_pages = int(sum(max((int(w.seq_lens[w.Rd + r]) - 1) // 128, 0) for r in range(w.Rp)))
-    pre_bytes = pre_pages * 8704 + w.n_prefill_rows * w.H * (128 + 64)
+    pre_bytes = pre_pages * 8704 + w.n_prefill_rows * w.H * (qb + 64)
     return dict(dec_bytes=dec_bytes, dec_pages=dec_pages, pre_flops=pre_flops,
                 pre_bytes=pre_bytes, pre_pages=pre_pages)
 
@@ -128,7 +133,8 @@ def cpu_baseline(w, budget_s):
             t0 = time.perf_counter()
             bt = np.arange(pages.shape[0], dtype=np.int32)[None, :]
             oracle.oracle_decode(w.q_codes[nreq * w.query_len:(nreq + 1) * w.query_len], pages,
-                                 bt, w.dec_seq_lens[nreq:nreq + 1], w.query_len)
+                                 bt, w.dec_seq_lens[nreq:nreq + 1], w.query_len,
+                                 q_dtype=w.q_dtype)
             t += time.perf_counter() - t0
             nreq += 1
         sample_s += t
@@ -148,7 +154,7 @@ def cpu_baseline(w, budget_s):
         while n < new and t_pages + t_rows < budget_s - sample_s:
             m = min(256, new - n)
             t0 = time.perf_counter()
-            oracle.index_rows(oracle.e4m3fn_to_float(w.q_codes[T0 + n:T0 + n + m]),
+            oracle.index_rows(oracle.q_values(w.q_codes[T0 + n:T0 + n + m], w.q_dtype),
                               pos_all[n:n + m], kp, 1.0)
             t_rows += time.perf_counter() - t0
             n += m
@@ -297,7 +303,7 @@ def main():
     from workloads.device import DeviceWorkload
 
     torch.cuda.set_device(0)
-    w = W.make_workload(a.workload, a.seed)
+    w = W.make_workload(a.workload, a.seed, q_dtype=a.q_dtype)
     print(f"[bench] staging {a.workload}: T={w.T} H={w.H} pages={w.num_blocks} "
           f"x{a.pool_copies} copies", file=sys.stderr, flush=True)
     dw = DeviceWorkload(w, m.mi_idx_insert_mxfp4, pool_copies=a.pool_copies)
@@ -347,6 +353,7 @@ def main():
     alg = algorithmic(w)
     dec_gbps = alg["dec_bytes"] / (dec_ms * 1e-3) / 1e9 if w.Rd else 0.0
     pre_tflops = alg["pre_flops"] / (pre_ms * 1e-3) / 1e12 if w.Rp else 0.0
+    peak_mfma = PEAK_BF16_TFLOPS if w.q_dtype == "bf16" else PEAK_FP8_TFLOPS
     phases = {
         "plan_ms": round(float(plan_ms), 4),
         "decode": {"kernel_ms": round(float(dec_ms), 4), "rows": w.n_decode_rows,
@@ -359,16 +366,18 @@ def main():
                     "index_k_GBps": round(alg["pre_bytes"] / (pre_ms * 1e-3) / 1e9, 1)
                     if w.Rp else None,
                     "tflops": round(pre_tflops, 1),
-                    "mfma_frac": round(pre_tflops / PEAK_FP8_TFLOPS, 4),
+                    "mfma_frac": round(pre_tflops / peak_mfma, 4),
                     "rows_per_s": round(w.n_prefill_rows / (pre_ms * 1e-3), 1) if w.Rp else None},
     }
     roof_dec = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
-                "traffic": measured_traffic("decode_score_kernel", "decode.hip"),
+                "traffic": (measured_traffic("decode_score_kernel", "decode.hip")
+                            if w.q_dtype == "e4m3" else None),
                 "kernel": "decode_score_kernel + decode_merge_kernel"}
-    roof_pre = {"bound": "mfma", "achieved": round(pre_tflops, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_FP8_TFLOPS, 4),
-                "traffic": measured_traffic("prefill_score_kernel", "prefill.hip"),
+    roof_pre = {"bound": "mfma", "achieved": round(pre_tflops, 1), "peak": peak_mfma,
+                "unit": "TFLOP/s", "frac": round(pre_tflops / peak_mfma, 4),
+                "traffic": (measured_traffic("prefill_score_kernel", "prefill.hip")
+                            if w.q_dtype == "e4m3" else None),
                 "kernel": "prefill_score_kernel"}
     dominant = roof_pre if (w.Rp and pre_ms >= dec_ms) else roof_dec
     res = {
@@ -382,9 +391,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 x fp4e2m1 (e8m0 scales) -> f32",
+        "dtype": ("bf16 x fp4e2m1 (e8m0 scales, converted to bf16) -> f32" if w.q_dtype == "bf16"
+                  else "fp8e4m3 x fp4e2m1 (e8m0 scales) -> f32"),
         "data": "synthetic",
-        "config": {"workload": a.workload, "seed": a.seed, "T": w.T, "heads": w.H,
+        "config": {"workload": a.workload, "seed": a.seed, "q_dtype": w.q_dtype, "T": w.T,
+                   "heads": w.H,
                    "decode_requests": w.Rd, "query_len": w.query_len,
                    "prefill_requests": w.Rp, "prefill_rows": w.n_prefill_rows,
                    "pool_pages": w.num_blocks, "pool_copies": a.pool_copies},
