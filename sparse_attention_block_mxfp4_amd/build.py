@@ -22,21 +22,47 @@ def hipcc():
     return exe
 
 
-def build(verbose=False, extra=()):
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           # device code: no NaN operands reach max/compare (keys test NaN on
-           # the bits), MFMA results stay in VGPRs
-           "-Xarch_device", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
-           "-I", os.path.join(ROOT, "include"), *extra, *srcs, "-o", tmp]
+# Per-source code-generation flags.  The prefill scorer is scheduled for
+# instruction-level parallelism (measured ~1.6 % faster on the mixed step; the
+# decode scorer is slightly slower with it and keeps the default scheduler).
+PER_SOURCE = {"prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
+def _flags():
+    return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # device code: no NaN operands reach max/compare (keys test NaN on
+            # the bits), MFMA results stay in VGPRs
+            "-Xarch_device", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
+            "-I", os.path.join(ROOT, "include")]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
+
+
+def build(verbose=False, extra=()):
+    """Compile every source (one object each, with its own flags) and link
+    them into libmi_idx.so; the library is replaced only when all succeed."""
+    from concurrent.futures import ThreadPoolExecutor
+    tmp = LIB + ".tmp"
+    objs = [os.path.join(HERE, "_build_" + name.replace(".hip", ".o")) for name in SOURCES]
+    try:
+        cmds = [[hipcc(), *_flags(), *PER_SOURCE.get(name, []), *extra, "-c",
+                 os.path.join(HERE, "csrc", name), "-o", obj] for name, obj in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     os.replace(tmp, LIB)
     return LIB
 
