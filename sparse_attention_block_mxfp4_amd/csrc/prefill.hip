@@ -91,10 +91,12 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   // thread t at [i][t] (consecutive lanes, consecutive words).
   __shared__ uint64_t s_queue[kQueue][NS * 64 * (16 / CGW)];
   // Drain requests, double-buffered by step parity: a wave whose queues may
-  // fill up at the next step posts a flag; at that step every wave of the
-  // workgroup drains, so one slow step serves all waves (the step barrier
-  // would make the others wait anyway).
-  __shared__ uint32_t s_need[2][NS * (16 / CGW)];
+  // fill up at the next step posts a flag byte; at that step every wave of
+  // the workgroup drains, so one slow step serves all waves (the step barrier
+  // would make the others wait anyway).  The 8 bytes of a parity are read as
+  // one word.
+  static_assert(NS * (16 / CGW) <= 8, "one flag byte per wave");
+  __shared__ __attribute__((aligned(8))) uint8_t s_need[2][8];
 
   if ((int)blockIdx.x >= plan[0]) return;
   const int4 tile = reinterpret_cast<const int4 *>(plan + kPreHeaderInts)[blockIdx.x];
@@ -197,9 +199,15 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   const uint32_t loff0 = 16u * (uint32_t)min(tid, kChunks);
   const uint32_t loff1 = 16u * (uint32_t)min(tid + NT, kChunks);
   const uint32_t loff2 = 16u * (uint32_t)min(tid + 2 * NT, kChunks);
-  auto pf_issue = [&](int step, uint4 &R0, uint4 &R1, uint4 &R2) {
-    const int jj = NS * step + stream;
-    const int phys = bt[min(jj, jlast)];
+  // Block-table entry of a step (clamped like the page index).
+  auto bt_entry = [&](int step) { return bt[min(NS * step + stream, jlast)]; };
+  // The entries of steps step and step + 1 as one vector load (even lanes the
+  // first, odd lanes the second), fetched a block before they are used: a
+  // vector load waits on the in-order load counter, which the page loads of
+  // the block in between have already drained, whereas a scalar load here
+  // would be waited for together with every outstanding LDS access.
+  auto bt_fetch = [&](int step) -> int { return bt_entry(step + (lane & 1)); };
+  auto pf_issue = [&](int step, int phys, uint4 &R0, uint4 &R1, uint4 &R2) {
     const bool valid = phys >= 0 && (int64_t)phys < num_blocks;
     const uint64_t bit = 1ull << (step & 63);
     vmask = valid ? (vmask | bit) : (vmask & ~bit);
@@ -322,12 +330,13 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   };
   // At the start of a step (parity = the step's): drain every queue if any
   // wave posted a flag in the previous step.
-  auto maybe_drain = [&](int parity) {
-    bool drain_now = false;
-#pragma unroll
-    for (int w = 0; w < NS * NW; ++w) drain_now = drain_now || s_need[parity ^ 1][w] != 0u;
-    if (__builtin_amdgcn_readfirstlane(drain_now ? 1 : 0)) drain();   // same for every lane
+  auto need_flags = [&](int parity) -> uint64_t {
+    return *reinterpret_cast<const uint64_t *>(&s_need[parity ^ 1][0]);
   };
+  auto drain_if = [&](uint64_t flags) {
+    if (__builtin_amdgcn_readfirstlane(flags != 0ull ? 1 : 0)) drain();   // same for every lane
+  };
+  auto maybe_drain = [&](int parity) { drain_if(need_flags(parity)); };
   auto take = [&](float v, int step, int parity) {
     const int j = NS * step + stream;
     const bool ok = (j >= 0) & (j < myL) & (((vmask >> (step & 63)) & 1ull) != 0ull);
@@ -349,7 +358,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   // inside the queue.
   auto post = [&](int parity) {
     const bool need = __any(nq >= kQueue - 3);
-    if (lane == 0) s_need[parity][wave_id] = need ? 1u : 0u;
+    if (lane == 0) s_need[parity][wave_id] = need ? 1 : 0;
   };
 
   // Step k of the stream handles page NS * k + stream; a page index at or
@@ -367,32 +376,34 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       s_floor[0][stream][tid] = 0ull;
       s_floor[1][stream][tid] = 0ull;
     }
-    if (lane == 0) {
-      s_need[0][wave_id] = 0u;
-      s_need[1][wave_id] = 0u;
-    }
-    pf_issue(0, e0, e1, e2);
+    if (threadIdx.x < 16) (&s_need[0][0])[threadIdx.x] = 0;
+    pf_issue(0, bt_entry(0), e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
-    pf_issue(1, o0, o1, o2);
+    pf_issue(1, bt_entry(1), o0, o1, o2);
     __builtin_amdgcn_sched_barrier(0);
     pf_commit(0, e0, e1, e2);
     pf_commit(1, o0, o1, o2);
     __builtin_amdgcn_sched_barrier(0);
-    pf_issue(2, e0, e1, e2);
+    pf_issue(2, bt_entry(2), e0, e1, e2);
     __builtin_amdgcn_sched_barrier(0);
-    pf_issue(3, o0, o1, o2);
+    pf_issue(3, bt_entry(3), o0, o1, o2);
     __builtin_amdgcn_sched_barrier(0);
+    int bt_a = bt_fetch(4), bt_b = 0;
     lds_barrier();
     // Blocks of two steps, one barrier each.  Block b reads steps 2b, 2b+1
     // from buffers (2b) & 3, (2b+1) & 3, commits steps 2b+2, 2b+3 (loaded
     // during block b-1) into the other two buffers, and issues the loads of
     // steps 2b+4, 2b+5.  A buffer is rewritten one barrier after its reads.
-    auto block = [&](int k, int rb, int parity) {
-      maybe_drain(parity);
+    // bt_use holds the block-table entries of steps k+4, k+5 (fetched one
+    // block earlier); bt_next receives those of steps k+6, k+7.
+    auto block = [&](int k, int rb, int parity, int bt_use, int &bt_next) {
+      const uint64_t flags = need_flags(parity);
       pf_commit(rb ^ 2, e0, e1, e2);
       pf_commit((rb ^ 2) + 1, o0, o1, o2);
-      pf_issue(k + 4, e0, e1, e2);
-      pf_issue(k + 5, o0, o1, o2);
+      bt_next = bt_fetch(k + 6);
+      pf_issue(k + 4, __builtin_amdgcn_readlane(bt_use, 0), e0, e1, e2);
+      pf_issue(k + 5, __builtin_amdgcn_readlane(bt_use, 1), o0, o1, o2);
+      drain_if(flags);
       if (stream == 0) {
         page_fold(rb, ma);
         pin(ma);
@@ -415,8 +426,8 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     };
     int k = 0;
     for (; k < K; k += 4) {
-      block(k, 0, 0);
-      block(k + 2, 2, 1);
+      block(k, 0, 0, bt_a, bt_b);
+      block(k + 2, 2, 1, bt_b, bt_a);
     }
     maybe_drain(0);
     take(page_reduce(mb), k - 1, 0);
