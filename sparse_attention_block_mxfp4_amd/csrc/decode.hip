@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     int capacity, int rows, int32_t *__restrict__ plan, uint8_t *__restrict__ ws) {
   constexpr int kWaves = kPlanThreads / 64;
   __shared__ long long s_wave[2][kWaves];
+  __shared__ long long s_first[kPlanThreads];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int2 *req_info = reinterpret_cast<int2 *>(ws + kWsHeaderBytes);
   // Contiguous segment of requests per thread.
@@ -113,16 +114,43 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     total_items += s_wave[1][w];
   }
   int4 *items = reinterpret_cast<int4 *>(plan + kPlanHeaderInts);
-  for (int r = r0; r < r1; ++r) {
-    const int h = history_of(seq_lens, r, max_pages);
-    const int c = chunk_of(h);
-    const int n = max(1, (h + c - 1) / c);
-    for (int i = 0; i < n; ++i) {
-      const long long it = first + i;
-      if (it < capacity) items[it] = make_int4(r, min(h, i * c), min(h, (i + 1) * c), 0);
+  if (per == 1) {
+    // One request per thread: the request's items are written by a team of
+    // tpr threads (consecutive threads, consecutive items), so the stores
+    // are spread over every wave and coalesced.
+    if (tid < num_reqs) {
+      const int h = history_of(seq_lens, tid, max_pages);
+      const int c = chunk_of(h);
+      const int n = max(1, (h + c - 1) / c);
+      s_first[tid] = first;
+      req_info[tid] = make_int2((int)first, n);
     }
-    req_info[r] = make_int2((int)first, n);
-    first += n;
+    __syncthreads();
+    int tpr = 1;
+    while (tpr * 2 * num_reqs <= kPlanThreads) tpr *= 2;
+    const int r = tid / tpr, sub = tid - r * tpr;
+    if (r < num_reqs) {
+      const int h = history_of(seq_lens, r, max_pages);
+      const int c = chunk_of(h);
+      const int n = max(1, (h + c - 1) / c);
+      const long long f = s_first[r];
+      for (int i = sub; i < n; i += tpr) {
+        const long long it = f + i;
+        if (it < capacity) items[it] = make_int4(r, min(h, i * c), min(h, (i + 1) * c), 0);
+      }
+    }
+  } else {
+    for (int r = r0; r < r1; ++r) {
+      const int h = history_of(seq_lens, r, max_pages);
+      const int c = chunk_of(h);
+      const int n = max(1, (h + c - 1) / c);
+      for (int i = 0; i < n; ++i) {
+        const long long it = first + i;
+        if (it < capacity) items[it] = make_int4(r, min(h, i * c), min(h, (i + 1) * c), 0);
+      }
+      req_info[r] = make_int2((int)first, n);
+      first += n;
+    }
   }
   if (tid == 0) {
     plan[0] = (int)min(total_items, (long long)capacity);
