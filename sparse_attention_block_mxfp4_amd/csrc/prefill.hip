@@ -396,22 +396,30 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // steps 2b+4, 2b+5.  A buffer is rewritten one barrier after its reads.
     // bt_use holds the block-table entries of steps k+4, k+5 (fetched one
     // block earlier); bt_next receives those of steps k+6, k+7.
+    // The staging (commit of steps k+2, k+3, issue of k+4, k+5) sits where
+    // the stream's LDS traffic is light: stream 1 opens with a selection
+    // step and stages first; stream 0 opens with its first page's operand
+    // reads (which would queue behind the staging writes) and stages after
+    // that page.
     auto block = [&](int k, int rb, int parity, int bt_use, int &bt_next) {
-      const uint64_t flags = need_flags(parity);
-      pf_commit(rb ^ 2, e0, e1, e2);
-      pf_commit((rb ^ 2) + 1, o0, o1, o2);
-      bt_next = bt_fetch(k + 6);
-      pf_issue(k + 4, __builtin_amdgcn_readlane(bt_use, 0), e0, e1, e2);
-      pf_issue(k + 5, __builtin_amdgcn_readlane(bt_use, 1), o0, o1, o2);
-      drain_if(flags);
+      auto stage = [&]() {
+        pf_commit(rb ^ 2, e0, e1, e2);
+        pf_commit((rb ^ 2) + 1, o0, o1, o2);
+        bt_next = bt_fetch(k + 6);
+        pf_issue(k + 4, __builtin_amdgcn_readlane(bt_use, 0), e0, e1, e2);
+        pf_issue(k + 5, __builtin_amdgcn_readlane(bt_use, 1), o0, o1, o2);
+      };
+      maybe_drain(parity);
       if (stream == 0) {
         page_fold(rb, ma);
         pin(ma);
         take(page_reduce(mb), k - 1, parity);
+        stage();
         page_fold(rb + 1, mb);
         pin(mb);
         take(page_reduce(ma), k, parity);
       } else {
+        stage();
         take(page_reduce(mb), k - 1, parity);
         pin(mb);
         page_fold(rb, ma);
