@@ -88,16 +88,30 @@ def algorithmic(w):
                 pre_bytes=pre_bytes, pre_pages=pre_pages)
 
 
+def source_digest(name):
+    """Digest of a kernel source and the header it includes, with comments and
+    whitespace removed: it changes when the code does, not when a comment
+    does."""
+    import hashlib
+    import re
+    csrc = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc")
+    text = ""
+    for f in (name, "common.h"):
+        text += open(os.path.join(csrc, f)).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256("".join(text.split()).encode()).hexdigest()[:16]
+
+
 def measured_traffic(kernel, source):
     """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, scaled by the
     copy calibration) from the committed rocprofv3 summary, or None when the
     kernel's source has changed since the counters were taken."""
-    import hashlib
     summary = os.path.join(ROOT, "profiles", "mixed_step_kernels.txt")
     src = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc", source)
     if not (os.path.exists(summary) and os.path.exists(src)):
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    digest = source_digest(source)
     for line in open(summary):
         f = line.split()
         if len(f) == 4 and f[0] == kernel and f[3] == digest:
@@ -205,7 +219,6 @@ def summarize_profiles(d, workload):
     """Write profiles/<workload>_kernels.txt from the rocprofv3 CSVs under d."""
     import collections
     import csv
-    import hashlib
 
     def counters(path):
         out = collections.defaultdict(list)
@@ -218,9 +231,7 @@ def summarize_profiles(d, workload):
                 if (kernel in k if part else k.startswith(kernel)) and c == counter]
         return sum(vals[0]) / len(vals[0]) if vals else None
 
-    def sha(name):
-        path = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc", name)
-        return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    sha = source_digest
 
     stats = list(csv.DictReader(open(os.path.join(d, "prof_trace", "trace_kernel_stats.csv"))))
     fetch = counters(os.path.join(d, "prof_fetch", "fetch_counter_collection.csv"))
@@ -246,7 +257,7 @@ def summarize_profiles(d, workload):
                                                    float(row["AverageNs"]), row["MinNs"],
                                                    row["MaxNs"]))
     out += ["", "## HBM traffic per launch (counter KiB x 1024 x calibration factor)",
-            "%-24s %16s %16s %s" % ("kernel", "fetch_bytes", "write_bytes", "source_sha256[:16]")]
+            "%-24s %16s %16s %s" % ("kernel", "fetch_bytes", "write_bytes", "source_digest")]
     for k in ["decode_plan_kernel", "decode_score_kernel", "decode_merge_kernel",
               "prefill_score_kernel"]:
         fv, wv = per_kernel(fetch, k, "FETCH_SIZE"), per_kernel(write, k, "WRITE_SIZE")

@@ -174,13 +174,15 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   int nq = 0;
   const int qslot = stream * NT + tid;
 
-  // Page pipeline.  Page p's 16-byte chunks are staged in register slot
-  // p & 1 (kLoads chunks per thread), copied into LDS buffer p & 1, and
-  // consumed from there by all the waves.  While page j is consumed, pages
-  // j+2 and j+3 are in flight and page j+1 already sits in the other LDS
-  // buffer.  Every load is unconditional (chunk and page indices are clamped,
-  // an invalid page id reads page 0 and is skipped), and the barriers order
-  // LDS only, so the global loads stay in flight across them.
+  // Page pipeline (per stream; step s is the stream's s-th page).  The
+  // 16-byte chunks of step s are loaded into register slot s & 1 (kLoads
+  // chunks per thread), copied into LDS buffer s & 3 a block later, and read
+  // there by the stream's four waves in the block after that: while a block
+  // consumes two pages, the next two sit in registers (then LDS) and the two
+  // after them are in flight.  Every load is unconditional (chunk and page
+  // indices are clamped, an invalid page id reads page 0 and is skipped), and
+  // the barriers order LDS only, so the global loads stay in flight across
+  // them.
   const int32_t *bt = block_table + (int64_t)r * bt_stride;
   const int jlast = J - 1;
   static_assert(kLoads >= 1 && kLoads <= 3, "page staging takes 1..3 chunks per thread");
