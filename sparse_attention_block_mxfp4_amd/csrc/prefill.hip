@@ -399,10 +399,10 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // bt_use holds the block-table entries of steps k+4, k+5 (fetched one
     // block earlier); bt_next receives those of steps k+6, k+7.
     // The staging (commit of steps k+2, k+3, issue of k+4, k+5) sits where
-    // the stream's LDS traffic is light: stream 1 opens with a selection
-    // step and stages first; stream 0 opens with its first page's operand
-    // reads (which would queue behind the staging writes) and stages after
-    // that page.
+    // the stream's LDS traffic is light: stream 1 stages after its opening
+    // selection step, before its first page's operand reads; stream 0 opens
+    // with those reads (which would queue behind the staging writes) and
+    // stages after its first page.
     auto block = [&](int k, int rb, int parity, int bt_use, int &bt_next) {
       auto stage = [&]() {
         pf_commit(rb ^ 2, e0, e1, e2);
@@ -421,9 +421,9 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         pin(mb);
         take(page_reduce(ma), k, parity);
       } else {
-        stage();
         take(page_reduce(mb), k - 1, parity);
         pin(mb);
+        stage();
         page_fold(rb, ma);
         pin(ma);
         take(page_reduce(ma), k, parity);
