@@ -124,7 +124,6 @@ struct TopList {
 #pragma unroll
     for (int i = 0; i < kHist; ++i) k[i] = 0ull;
   }
-  __device__ __forceinline__ uint64_t threshold() const { return k[kHist - 1]; }
   // Insert x with no branch (x = 0 leaves the list unchanged), so the caller's
   // basic block stays whole for the scheduler.
   __device__ __forceinline__ void insert_nb(uint64_t x) {
@@ -174,58 +173,6 @@ __device__ __forceinline__ float max_split16(float a, float b) {
                                                   false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-// A top-15 list with a 4-slot per-lane pending buffer: a key that beats the
-// list's current 15th key is shifted into the buffer (a few selects, no
-// branch); when any lane of the wave has a full buffer, every lane's buffer
-// is inserted into its list.  Early on almost every page qualifies, later
-// only a few, so most pages cost ~10 VALU instead of a full insertion.
-struct PendingTop {
-  TopList top;
-  uint64_t p0, p1, p2, p3;
-  int n;
-  __device__ __forceinline__ void clear() {
-    top.clear();
-    p0 = p1 = p2 = p3 = 0ull;
-    n = 0;
-  }
-  __device__ __forceinline__ void flush() {
-    top.insert_nb(p0);
-    top.insert_nb(p1);
-    top.insert_nb(p2);
-    top.insert_nb(p3);
-    p0 = p1 = p2 = p3 = 0ull;
-    n = 0;
-  }
-  // Shift key into the buffer if it beats the list's 15th key (no branch).
-  __device__ __forceinline__ void push_only(uint64_t key) {
-    const bool c = key > top.k[kHist - 1];
-    p3 = c ? p2 : p3;
-    p2 = c ? p1 : p2;
-    p1 = c ? p0 : p1;
-    p0 = c ? key : p0;
-    n += c ? 1 : 0;
-  }
-  // As push_only, with an extra bound: keys at or below `floor` are dropped
-  // (a lower bound on the final 15th key known from elsewhere).
-  __device__ __forceinline__ void push_only(uint64_t key, uint64_t floor) {
-    const uint64_t t = top.k[kHist - 1] > floor ? top.k[kHist - 1] : floor;
-    const bool c = key > t;
-    p3 = c ? p2 : p3;
-    p2 = c ? p1 : p2;
-    p1 = c ? p0 : p1;
-    p0 = c ? key : p0;
-    n += c ? 1 : 0;
-  }
-  // Keep room for the next key: flush once any lane's buffer is full.
-  __device__ __forceinline__ void make_room() {
-    if (__any(n == 4)) flush();
-  }
-  __device__ __forceinline__ void push(uint64_t key) {
-    push_only(key);
-    make_room();
-  }
-};
 
 // Workgroup barrier that orders LDS accesses only: global loads in flight
 // stay in flight across it.

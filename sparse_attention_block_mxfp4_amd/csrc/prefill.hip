@@ -22,14 +22,8 @@ constexpr int kTileCols = 256;          // query columns per workgroup
 constexpr int kPreHeaderInts = 16;
 constexpr int kChunks = kPageBytes / 16;                    // 544 16-byte chunks
 constexpr int kXcds = 8;                // MI355X accelerator complex dies
-#ifndef MI_IDX_PREFILL_CGW
-#define MI_IDX_PREFILL_CGW 4
-#endif
-constexpr int kPrefillCgw = MI_IDX_PREFILL_CGW;   // 16-column groups per wave
-#ifndef MI_IDX_PREFILL_STREAMS
-#define MI_IDX_PREFILL_STREAMS 2
-#endif
-constexpr int kPrefillStreams = MI_IDX_PREFILL_STREAMS;   // page streams per workgroup
+constexpr int kPrefillCgw = 4;          // 16-column groups per wave
+constexpr int kPrefillStreams = 2;      // page streams per workgroup
 constexpr int kQueue = 16;              // per-column key queue (LDS)
 constexpr int kBufs = 4;                // LDS page buffers per stream
 
@@ -43,17 +37,8 @@ inline int rows_per_tile(int H) { return kTileCols / H; }
 // max over its tokens, so any assignment that covers the 128 tokens once is
 // correct; the one chosen spreads a tile's LDS reads (dword 17*token + 4*g)
 // over distinct banks.
-#ifndef MI_IDX_TOKEN_MAP
-#define MI_IDX_TOKEN_MAP 32
-#endif
 __device__ __forceinline__ int page_token(int tl, int t16) {
-#if MI_IDX_TOKEN_MAP == 64
-  return 64 * (tl >> 2) + 16 * (t16 >> 2) + 4 * (tl & 3) + (t16 & 3);
-#elif MI_IDX_TOKEN_MAP == 32
   return 32 * (tl >> 1) + 8 * (t16 >> 2) + 4 * (tl & 1) + (t16 & 3);
-#else
-  return tl * 16 + t16;
-#endif
 }
 
 // CGW = 16-column MFMA groups per wave: 16 / CGW waves cover the tile's
