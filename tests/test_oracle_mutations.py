@@ -7,8 +7,10 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import forced as FO
 from oracle import formats as F
 from oracle import indexer as I
+from tests import test_oracle_forced as TFO
 from tests import test_oracle_formats as TF
 from tests import test_oracle_indexer as TI
 from tests import test_oracle_plan as TP
@@ -31,6 +33,9 @@ PINS = [
     TI.test_nan_scores_rank_last,
     TI.test_prefill_row_equals_decode_row_at_same_position,
     TP.test_chunks_against_bruteforce_and_properties,
+    TFO.test_bruteforce_tiny_rows,
+    TFO.test_special_cases,
+    TFO.test_output_form,
 ]
 
 
@@ -164,6 +169,33 @@ def _encode_exp_minus_one(rows, chunk=8192):
 
 _orig_chunks = oracle.prefill_chunks
 
+_orig_windows = FO.forced_windows
+_orig_forced = FO.select_forced_row
+
+
+def _forced_select_ties_high(scores, L, topk, init_blocks, local_blocks, max_k_tiles):
+    s = np.asarray(scores, dtype=np.float64)
+    out = np.full(topk, -1, dtype=np.int32)
+    if L < 0:
+        return out
+    nvp = L + 1
+    if nvp <= topk:
+        out[:nvp] = np.arange(nvp)
+        return out
+    fb, fe = _orig_windows(L, topk, init_blocks, local_blocks, max_k_tiles)
+    cand = list(range(fb, nvp - fe))
+    cand.sort(key=lambda j: (np.isnan(s[j]), -s[j] if not np.isnan(s[j]) else 0.0, -j))
+    sel = sorted(list(range(fb)) + list(range(nvp - fe, nvp)) + cand[:topk - fb - fe])
+    out[:len(sel)] = sel
+    return out
+
+
+def _forced_descending(scores, L, topk, init_blocks, local_blocks, max_k_tiles):
+    out = _orig_forced(scores, L, topk, init_blocks, local_blocks, max_k_tiles)
+    ids = out[out >= 0][::-1]
+    out[:len(ids)] = ids
+    return out
+
 
 MUTATIONS = {
     "nibbles_swapped": [(I, "decode_pages", _decode_pages_swapped_nibbles)],
@@ -188,6 +220,15 @@ MUTATIONS = {
                                     (oracle, "mxfp4_encode_rows", _encode_exp_minus_one)],
     "chunks_overfill": [(oracle, "prefill_chunks",
                          lambda s, b: _orig_chunks(s, b + 1))],
+    "forced_end_window_one_wider": [(FO, "forced_windows",
+                                     lambda L, k, i, l, m: (lambda fb, fe: (fb, min(fe + 1, k - fb)))(
+                                         *_orig_windows(L, k, i, l, m)))],
+    "forced_begin_ignores_max_k_tiles": [(FO, "forced_windows",
+                                          lambda L, k, i, l, m: _orig_windows(L, k, i, l, 10 ** 9))],
+    "forced_ties_to_higher_id": [(FO, "select_forced_row", _forced_select_ties_high),
+                                 (oracle, "select_forced_row", _forced_select_ties_high)],
+    "forced_output_descending": [(FO, "select_forced_row", _forced_descending),
+                                 (oracle, "select_forced_row", _forced_descending)],
 }
 
 
