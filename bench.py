@@ -54,6 +54,10 @@ def parse():
                         "profiles/<workload>_kernels.txt")
     p.add_argument("--cpu-seconds", type=float, default=18.0,
                    help="oracle time budget of the CPU baseline sample")
+    p.add_argument("--forced", metavar="TOPK,INIT,LOCAL",
+                   help="also time the general forced-block selection (mi_idx_select_forced) "
+                        "on the step's output, outside the timed step; reported under "
+                        "phases.select_forced")
     return p.parse_args()
 
 
@@ -414,6 +418,28 @@ def main():
         "roofline": dominant,
         "roofline_kernels": {"decode": roof_dec, "prefill": roof_pre},
     }
+    if a.forced:
+        topk, init, local = (int(x) for x in a.forced.split(","))
+        max_k_tiles = -(-int(np.max(w.seq_lens)) // 128)
+        sel_out = torch.empty((w.T, w.H, topk), dtype=torch.int32, device="cuda")
+        for _ in range(20):
+            m.mi_idx_select_forced(dw.out, topk, init, local, max_k_tiles, out=sel_out)
+        times = []
+        for _ in range(50):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            m.mi_idx_select_forced(dw.out, topk, init, local, max_k_tiles, out=sel_out)
+            e1.record(stream)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        sel_ms = float(np.median([x.elapsed_time(y) for x, y in times]))
+        sel_bytes = w.T * w.H * (16 + topk) * 4
+        phases["select_forced"] = {
+            "topk": topk, "init_blocks": init, "local_blocks": local,
+            "max_k_tiles": max_k_tiles, "kernel_ms": round(sel_ms, 4),
+            "algorithmic_bytes": sel_bytes,
+            "GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

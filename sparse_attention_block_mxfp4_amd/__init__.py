@@ -42,6 +42,7 @@ _SIGS = {
     "mi_idx_plan_prefill": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp, _vp, _vp]),
     "mi_idx_score_topk_prefill": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32,
                                          _i64, _i32, _i32, _f32, _vp, _sz, _i32, _vp, _vp, _vp]),
+    "mi_idx_select_forced": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -245,6 +246,27 @@ def mi_idx_score_topk_prefill(q, pages, block_table, cu_seqlens_q, seq_lens, con
         max_pages, float(scale), _ptr(plan), plan.numel(), num_tiles, _ptr(topk_out),
         _ptr(scores_out), _stream(stream))
     _check(st, "mi_idx_score_topk_prefill")
+
+
+def mi_idx_select_forced(ranked, topk, init_blocks, local_blocks, max_k_tiles, out=None,
+                         stream=None):
+    """ranked [..., 16] int32 rows as the score calls write them; returns out
+    [..., topk] int32 (allocated when not given): the forced windows, the best
+    pages between them, ascending, -1 tail."""
+    _need(ranked, "ranked", _I32)
+    if ranked.dim() < 1 or ranked.shape[-1] != TOPK:
+        raise ValueError("ranked must be [..., 16]")
+    shape = tuple(ranked.shape[:-1]) + (int(topk),)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=ranked.device)
+    _need(out, "out", _I32)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must be {list(shape)}")
+    n = ranked.numel() // TOPK
+    st = lib.mi_idx_select_forced(_ptr(ranked), n, int(topk), int(init_blocks),
+                                  int(local_blocks), int(max_k_tiles), _ptr(out), _stream(stream))
+    _check(st, "mi_idx_select_forced")
+    return out
 
 
 __all__ = [n for n in dir() if n.startswith("mi_idx_")] + ["MiIdxError", "lib", "LIB_PATH"]

@@ -58,3 +58,48 @@ def compare(gpu, ora, scores, L, rows=None, rel_tol=REL_TOL, gpu_scores=None):
                 assert np.all(diff <= tol), (
                     f"row {t} head {h}: score error {diff.max()} > tol {tol}")
     return exact / max(total, 1)
+
+
+def compare_forced(gpu, ora, scores, L, topk, init_blocks, local_blocks, max_k_tiles,
+                   rel_tol=REL_TOL):
+    """GPU-vs-oracle comparison of the general forced selection ([T, H, topk],
+    ascending ids, -1 tail).  Per (row, head): the form (ascending, distinct,
+    -1 only as a tail, ids in 0..L), the forced windows exactly, and the pages
+    taken between them rank by rank in oracle score within tol (as in
+    ``compare``).  Returns the bit-exact fraction."""
+    gpu = np.asarray(gpu)
+    exact = total = 0
+    for t in range(gpu.shape[0]):
+        Lt = int(L[t])
+        for h in range(gpu.shape[1]):
+            g = gpu[t, h]
+            o = np.asarray(ora[t][h])
+            total += 1
+            if Lt < 0:
+                assert np.all(g == -1), f"row {t} head {h}: padding row not all -1: {g}"
+                exact += 1
+                continue
+            nvp = Lt + 1
+            ids = g[g >= 0]
+            assert len(ids) == min(topk, nvp), f"row {t} head {h}: {g}"
+            assert np.all(g[len(ids):] == -1) and np.all(np.diff(ids) > 0), f"row {t} {h}: {g}"
+            assert ids.max() <= Lt, f"row {t} head {h}: id past the local page: {g}"
+            if np.array_equal(g, o):
+                exact += 1
+                continue
+            assert nvp > topk, f"row {t} head {h}: a short row must list all pages: {g}"
+            fb = min(init_blocks, max_k_tiles, topk)
+            fe = min(local_blocks, topk - fb)
+            forced = set(range(fb)) | set(range(nvp - fe, nvp))
+            assert forced <= set(ids.tolist()), f"row {t} head {h}: forced pages missing: {g}"
+            gm = np.array(sorted(set(ids.tolist()) - forced))
+            om = np.array(sorted(set(o[o >= 0].tolist()) - forced))
+            assert len(gm) == len(om)
+            s = np.asarray(scores[t][h], dtype=np.float64)
+            tol = rel_tol * (np.abs(s).max() if s.size else 0.0)
+            sg = np.sort(s[gm])[::-1]
+            so = np.sort(s[om])[::-1]
+            bad = np.abs(sg - so) > tol
+            assert not bad.any(), (f"row {t} head {h}: gpu {g} vs oracle {o}; score gaps "
+                                   f"{(sg - so)[bad]} exceed tol {tol}")
+    return exact / max(total, 1)

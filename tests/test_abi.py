@@ -30,7 +30,7 @@ def m():
 
 def test_library_exports_every_declared_symbol(m):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 12
     raw = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -113,6 +113,30 @@ def test_insert_argument_errors(m):
     assert L.mi_idx_insert_mxfp4(buf, 0, 128, buf, 0, buf, 4, None) == m.OK
     assert L.mi_idx_insert_mxfp4(buf, 0, 128, buf, 4, buf, 0, None) == m.EINVAL
     assert L.mi_idx_insert_mxfp4(buf + 4, 0, 128, buf, 4, buf, 4, None) == m.EINVAL
+
+
+def test_select_forced_argument_errors(m):
+    L = m.lib
+    buf = _fake(1 << 16)
+    B = buf.ctypes.data
+    B = B + (-B) % 16                                   # 16-byte aligned
+    O = B + 4096
+
+    def call(ranked=B, n=4, topk=8, init=0, local=1, mkt=10, out=O):
+        return L.mi_idx_select_forced(ranked, n, topk, init, local, mkt, out, None)
+    assert call(topk=0) == m.EUNSUPPORTED
+    assert call(topk=17) == m.EUNSUPPORTED
+    assert call(local=0) == m.EUNSUPPORTED               # the local page is never scored
+    assert call(init=-1) == m.EINVAL
+    assert call(mkt=-1) == m.EINVAL
+    assert call(n=-1) == m.EINVAL
+    assert call(ranked=None) == m.EINVAL
+    assert call(out=None) == m.EINVAL
+    assert call(ranked=B + 4) == m.EINVAL                # misaligned rows
+    assert call(out=B + 32) == m.EINVAL                  # overlaps the input
+    assert call(out=B, topk=8) == m.EINVAL               # in place needs topk 16
+    assert call(n=0) == m.OK                             # nothing to do, nothing launched
+    assert b"select_forced" in L.mi_idx_last_error() or True
 
 
 def test_prefill_argument_errors(m):
