@@ -10,7 +10,9 @@ import oracle
 from oracle import forced as FO
 from oracle import formats as F
 from oracle import indexer as I
+from oracle import normrope as NR
 from tests import test_oracle_forced as TFO
+from tests import test_oracle_normrope as TNR
 from tests import test_oracle_formats as TF
 from tests import test_oracle_indexer as TI
 from tests import test_oracle_plan as TP
@@ -36,6 +38,11 @@ PINS = [
     TFO.test_bruteforce_tiny_rows,
     TFO.test_special_cases,
     TFO.test_output_form,
+    TNR.test_rms_norm_closed_form,
+    TNR.test_rms_norm_properties,
+    TNR.test_rope_worked_examples,
+    TNR.test_rope_group_properties,
+    TNR.test_pairings_are_one_permutation_apart,
 ]
 
 
@@ -169,6 +176,49 @@ def _encode_exp_minus_one(rows, chunk=8192):
 
 _orig_chunks = oracle.prefill_chunks
 
+_orig_rms = NR.rms_norm
+_orig_rope = NR.rope
+
+
+def _rms_eps_outside(x, weight, eps):
+    x = np.asarray(x, dtype=np.float64)
+    if weight is None:
+        return x.copy()
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * weight
+
+
+def _rms_sum_not_mean(x, weight, eps):
+    x = np.asarray(x, dtype=np.float64)
+    if weight is None:
+        return x.copy()
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * weight
+
+
+def _rope_sin_flipped(x, positions, rotary_dim, base, style):
+    return _orig_rope(x, -np.asarray(positions, dtype=np.float64), rotary_dim, base, style)
+
+
+def _rope_half_frequency(x, positions, rotary_dim, base, style):
+    # exponent -i/rd instead of -2i/rd: the same as doubling rotary_dim in the frequencies
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    if rotary_dim == 0:
+        return out
+    i = np.arange(rotary_dim // 2)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * np.power(base, -1.0 * i / rotary_dim)
+    fa, fb = NR.rope_pairs(rotary_dim, style)
+    a, b = x[:, fa], x[:, fb]
+    out[:, fa] = a * np.cos(ang) - b * np.sin(ang)
+    out[:, fb] = b * np.cos(ang) + a * np.sin(ang)
+    return out
+
+
+def _rope_pairs_swapped(rotary_dim, style):
+    return _orig_pairs(rotary_dim, 1 - style)
+
+
+_orig_pairs = NR.rope_pairs
+
 _orig_windows = FO.forced_windows
 _orig_forced = FO.select_forced_row
 
@@ -229,6 +279,12 @@ MUTATIONS = {
                                  (oracle, "select_forced_row", _forced_select_ties_high)],
     "forced_output_descending": [(FO, "select_forced_row", _forced_descending),
                                  (oracle, "select_forced_row", _forced_descending)],
+    "rms_eps_outside_sqrt": [(NR, "rms_norm", _rms_eps_outside), (oracle, "rms_norm", _rms_eps_outside)],
+    "rms_sum_not_mean": [(NR, "rms_norm", _rms_sum_not_mean), (oracle, "rms_norm", _rms_sum_not_mean)],
+    "rope_sin_flipped": [(NR, "rope", _rope_sin_flipped), (oracle, "rope", _rope_sin_flipped)],
+    "rope_half_frequency": [(NR, "rope", _rope_half_frequency),
+                            (oracle, "rope", _rope_half_frequency)],
+    "rope_pairings_swapped": [(NR, "rope_pairs", _rope_pairs_swapped)],
 }
 
 
