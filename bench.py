@@ -54,6 +54,10 @@ def parse():
                         "profiles/<workload>_kernels.txt")
     p.add_argument("--cpu-seconds", type=float, default=18.0,
                    help="oracle time budget of the CPU baseline sample")
+    p.add_argument("--insert", action="store_true",
+                   help="also time the fused qk-norm / rotary / MXFP4 insert of the step's T "
+                        "new index-K rows (fp32, RMS norm, rotary dim 64 neox), outside the "
+                        "timed step; reported under phases.norm_rope_insert")
     p.add_argument("--forced", metavar="TOPK,INIT,LOCAL",
                    help="also time the general forced-block selection (mi_idx_select_forced) "
                         "on the step's output, outside the timed step; reported under "
@@ -418,6 +422,34 @@ def main():
         "roofline": dominant,
         "roofline_kernels": {"decode": roof_dec, "prefill": roof_pre},
     }
+    if a.insert:
+        n_ins = w.T
+        gen = torch.Generator(device="cuda").manual_seed(a.seed)
+        k_new = torch.randn((n_ins, 128), device="cuda", generator=gen)
+        wn = torch.rand(128, device="cuda", generator=gen) + 0.5
+        pos_new = torch.randint(0, 1 << 20, (n_ins,), device="cuda", generator=gen)
+        ins_pages = torch.zeros(((n_ins + 127) // 128) * 8704, dtype=torch.uint8, device="cuda")
+        slot_new = torch.randperm(n_ins, device="cuda", generator=gen)
+        call = lambda: m.mi_idx_norm_rope_insert_mxfp4(  # noqa: E731
+            k_new, slot_new, ins_pages, norm_weight=wn, norm_eps=1e-6, positions=pos_new,
+            rotary_dim=64, rope_base=10000.0, rope_style=0)
+        for _ in range(20):
+            call()
+        times = []
+        for _ in range(50):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        ins_ms = float(np.median([x.elapsed_time(y) for x, y in times]))
+        ins_bytes = n_ins * (128 * 4 + 68 + 8 + 8)
+        phases["norm_rope_insert"] = {
+            "rows": n_ins, "rotary_dim": 64, "kernel_ms": round(ins_ms, 4),
+            "algorithmic_bytes": ins_bytes,
+            "GBps": round(ins_bytes / (ins_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(ins_bytes / (ins_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
     if a.forced:
         topk, init, local = (int(x) for x in a.forced.split(","))
         max_k_tiles = -(-int(np.max(w.seq_lens)) // 128)

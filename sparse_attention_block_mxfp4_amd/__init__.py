@@ -43,6 +43,8 @@ _SIGS = {
     "mi_idx_score_topk_prefill": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32,
                                          _i64, _i32, _i32, _f32, _vp, _sz, _i32, _vp, _vp, _vp]),
     "mi_idx_select_forced": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "mi_idx_norm_rope_insert_mxfp4": (_i32, [_vp, _i32, _i64, _vp, _f32, _vp, _i32, _c.c_double,
+                                             _i32, _vp, _i64, _vp, _i64, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(lib, _name)
@@ -132,6 +134,38 @@ def mi_idx_insert_mxfp4(k, slot_mapping, pages, stream=None):
                                  _ptr(slot_mapping), k.shape[0], _ptr(pages), num_blocks,
                                  _stream(stream))
     _check(st, "mi_idx_insert_mxfp4")
+
+
+ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
+
+
+def mi_idx_norm_rope_insert_mxfp4(k, slot_mapping, pages, norm_weight=None, norm_eps=1e-6,
+                                  positions=None, rotary_dim=0, rope_base=10000.0,
+                                  rope_style=ROPE_NEOX, stream=None):
+    """As mi_idx_insert_mxfp4, with the rows first RMS-normalised (norm_weight
+    [128] fp32, or None for no norm) and their first rotary_dim dims rotated
+    at positions [n] int64."""
+    _need(k, "k", (torch.float32, torch.bfloat16), contiguous=False)
+    if k.dim() != 2 or k.shape[1] != HEAD_DIM or k.stride(1) != 1:
+        raise ValueError("k must be [n, 128] with unit column stride")
+    _need(slot_mapping, "slot_mapping", (torch.int64,))
+    _need(pages, "pages", _U8)
+    if slot_mapping.numel() != k.shape[0]:
+        raise ValueError("slot_mapping must have one entry per row of k")
+    if norm_weight is not None:
+        _need(norm_weight, "norm_weight", (torch.float32,))
+        if norm_weight.numel() != HEAD_DIM:
+            raise ValueError("norm_weight must have 128 entries")
+    if rotary_dim:
+        _need(positions, "positions", (torch.int64,))
+        if positions.numel() != k.shape[0]:
+            raise ValueError("positions must have one entry per row of k")
+    st = lib.mi_idx_norm_rope_insert_mxfp4(
+        _ptr(k), 0 if k.dtype == torch.float32 else 1, k.stride(0), _ptr(norm_weight),
+        float(norm_eps), _ptr(positions) if rotary_dim else None, int(rotary_dim),
+        float(rope_base), int(rope_style), _ptr(slot_mapping), k.shape[0], _ptr(pages),
+        pages.numel() // PAGE_BYTES, _stream(stream))
+    _check(st, "mi_idx_norm_rope_insert_mxfp4")
 
 
 def mi_idx_decode_plan_bytes(max_reqs):

@@ -103,3 +103,53 @@ def compare_forced(gpu, ora, scores, L, topk, init_blocks, local_blocks, max_k_t
             assert not bad.any(), (f"row {t} head {h}: gpu {g} vs oracle {o}; score gaps "
                                    f"{(sg - so)[bad]} exceed tol {tol}")
     return exact / max(total, 1)
+
+
+_E2M1_BOUNDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def compare_encoded(records, y, rel=1e-5):
+    """GPU-written MXFP4 token records [n, 68] against the exact (fp64) rows
+    y [n, 128] they encode.  Each block's scale byte must equal the oracle
+    encoder's, unless the block's amax is within ``rel`` of a power of two
+    (where the GPU's fp32 arithmetic may land on either side); each code must
+    equal the oracle's, unless the scaled value |y| / 2^X is within ``rel`` of
+    a rounding boundary between the two codes (same sign, adjacent
+    magnitudes) or both are zero.  Returns the bit-exact fraction of
+    records."""
+    import oracle
+    rec = np.asarray(records, dtype=np.uint8).reshape(-1, 68)
+    y = np.asarray(y, dtype=np.float64)
+    codes_o, sb_o = oracle.mxfp4_encode_rows(y)
+    cb = rec[:, :64].astype(np.int64)
+    codes_g = np.empty((rec.shape[0], 128), dtype=np.int64)
+    codes_g[:, 0::2] = cb & 0xF
+    codes_g[:, 1::2] = cb >> 4
+    sb_g = rec[:, 64:68].astype(np.int64)
+    exact = 0
+    for r in range(rec.shape[0]):
+        row_exact = True
+        for b in range(4):
+            blk = slice(32 * b, 32 * b + 32)
+            amax = np.abs(y[r, blk]).max()
+            if sb_g[r, b] != sb_o[r, b]:
+                row_exact = False
+                m = amax / 2.0 ** np.round(np.log2(amax)) if amax > 0 else 0.0
+                assert amax > 0 and abs(m - 1.0) <= rel, (
+                    f"row {r} block {b}: scale {sb_g[r, b]} vs {sb_o[r, b]}, amax {amax}")
+                continue
+            X = int(sb_o[r, b]) - 127
+            x = np.abs(y[r, blk]) / 2.0 ** X
+            for d in np.nonzero(codes_g[r, blk] != codes_o[r, blk])[0]:
+                row_exact = False
+                cg, co = int(codes_g[r, 32 * b + d]), int(codes_o[r, 32 * b + d])
+                if (cg & 7) == 0 and (co & 7) == 0:
+                    continue                                  # +0 / -0
+                assert (cg & 8) == (co & 8) and abs((cg & 7) - (co & 7)) == 1, (
+                    f"row {r} dim {32 * b + d}: code {cg} vs {co}, value {y[r, 32 * b + d]}")
+                bound = _E2M1_BOUNDS[min(cg & 7, co & 7)]
+                assert abs(x[d] - bound) <= rel * bound, (
+                    f"row {r} dim {32 * b + d}: code {cg} vs {co} away from a boundary "
+                    f"(scaled {x[d]})")
+        exact += row_exact
+    return exact / max(rec.shape[0], 1)

@@ -30,7 +30,7 @@ def m():
 
 def test_library_exports_every_declared_symbol(m):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     raw = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -113,6 +113,33 @@ def test_insert_argument_errors(m):
     assert L.mi_idx_insert_mxfp4(buf, 0, 128, buf, 0, buf, 4, None) == m.OK
     assert L.mi_idx_insert_mxfp4(buf, 0, 128, buf, 4, buf, 0, None) == m.EINVAL
     assert L.mi_idx_insert_mxfp4(buf + 4, 0, 128, buf, 4, buf, 4, None) == m.EINVAL
+
+
+def test_norm_rope_insert_argument_errors(m):
+    L = m.lib
+    buf = _fake(1 << 16)
+    B = buf.ctypes.data
+    B = B + (-B) % 16
+
+    def call(k=B, kd=0, stride=128, w=B, eps=1e-6, pos=B, rd=64, base=10000.0, style=0,
+             slots=B, n=4, pages=B, nb=4):
+        return L.mi_idx_norm_rope_insert_mxfp4(k, kd, stride, w, eps, pos, rd, base, style,
+                                               slots, n, pages, nb, None)
+    assert call(rd=12) == m.EUNSUPPORTED                 # not a multiple of 8
+    assert call(rd=136) == m.EUNSUPPORTED
+    assert call(style=2) == m.EINVAL
+    assert call(base=0.0) == m.EINVAL
+    assert call(base=float("inf")) == m.EINVAL
+    assert call(eps=-1.0) == m.EINVAL
+    assert call(eps=float("nan")) == m.EINVAL
+    assert call(pos=None) == m.EINVAL                    # rotation needs positions
+    assert call(w=B + 4) == m.EINVAL                     # misaligned weights
+    assert call(kd=3) == m.EINVAL
+    assert call(stride=100) == m.EINVAL
+    assert call(n=-1) == m.EINVAL
+    assert call(nb=0) == m.EINVAL
+    assert call(n=0) == m.OK
+    assert call(n=0, rd=0, pos=None, w=None) == m.OK     # a plain insert of nothing
 
 
 def test_select_forced_argument_errors(m):
