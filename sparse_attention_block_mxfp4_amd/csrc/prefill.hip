@@ -62,24 +62,25 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   static_assert(NS >= 1 && NS <= 2, "one or two page streams");
   static_assert(NS == 1 || kHist * NT * 8 <= NS * kBufs * kPageBytes,
                 "the stream merge reuses the page buffers");
-  // Two LDS page buffers per stream, each in the page's global byte layout
-  // (token t at 68*t).
-  // (+16 bytes: the landing slot of the threads that have no chunk to write)
+  // kBufs LDS page buffers per stream (a ring: two pages read per block while
+  // the next two are written), each in the page's global byte layout (token
+  // t at 68*t; +16 bytes: the landing slot of the threads that have no chunk
+  // to write).
   __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][kBufs][kPageBytes + 16];
-  // Each stream's current 15th key per column, double-buffered by step
-  // parity: step k writes slot k & 1 and reads the partner's slot written in
-  // step k-1 (a barrier apart).  Keys are distinct, so a key at or below the
+  // Each stream's current 15th key per column, double-buffered by block
+  // parity: block b writes slot b & 1 and reads the partner's slot written in
+  // block b-1 (a barrier apart).  Keys are distinct, so a key at or below the
   // partner's 15th key has 15 better keys there and cannot be in the final
   // top-15: the partner's bound filters this stream's pushes.
   __shared__ uint64_t s_floor[NS == 2 ? 2 : 1][NS][NS == 2 ? 64 * (16 / CGW) : 1];
   // Keys waiting to enter a column's list: a queue per thread, entry i of
   // thread t at [i][t] (consecutive lanes, consecutive words).
   __shared__ uint64_t s_queue[kQueue][NS * 64 * (16 / CGW)];
-  // Drain requests, double-buffered by step parity: a wave whose queues may
-  // fill up at the next step posts a flag byte; at that step every wave of
-  // the workgroup drains, so one slow step serves all waves (the step barrier
-  // would make the others wait anyway).  The 8 bytes of a parity are read as
-  // one word.
+  // Drain requests, double-buffered by block parity: at the end of a block a
+  // wave whose queues may fill up in the next block posts a flag byte; at the
+  // start of that block every wave of the workgroup drains, so one slow
+  // block serves all waves (the block barrier would make the others wait
+  // anyway).  The 8 bytes of a parity are read as one word.
   static_assert(NS * (16 / CGW) <= 8, "one flag byte per wave");
   __shared__ __attribute__((aligned(8))) uint8_t s_need[2][8];
 
@@ -303,9 +304,9 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       return max_xor16(max_xor32(m[0]));
     }
   };
-  // Offer page j's max to the column's list (j < 0 or past the row's
-  // history: nothing).  Branch-free; the caller makes room afterwards.
   const int wave_id = stream * NW + wave;
+  // Insert every queued key into its column's list; each wave runs as many
+  // insertions as its fullest queue holds.
   auto drain = [&]() {
 #pragma unroll 1
     for (int i = 0; i < kQueue; ++i) {
@@ -315,8 +316,8 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     }
     nq = 0;
   };
-  // At the start of a step (parity = the step's): drain every queue if any
-  // wave posted a flag in the previous step.
+  // At the start of a block (parity = the block's): drain every queue if
+  // any wave posted a flag at the end of the previous block.
   auto need_flags = [&](int parity) -> uint64_t {
     return *reinterpret_cast<const uint64_t *>(&s_need[parity ^ 1][0]);
   };
@@ -324,6 +325,9 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     if (__builtin_amdgcn_readfirstlane(flags != 0ull ? 1 : 0)) drain();   // same for every lane
   };
   auto maybe_drain = [&](int parity) { drain_if(need_flags(parity)); };
+  // Offer page j's max to the column's list (j < 0, past the row's history
+  // or an invalid page: nothing).  Branch-free: the queue write always
+  // happens, the count moves only for a key above the filter bound.
   auto take = [&](float v, int step, int parity) {
     const int j = NS * step + stream;
     const bool ok = (j >= 0) & (j < myL) & (((vmask >> (step & 63)) & 1ull) != 0ull);
@@ -334,8 +338,9 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       bound = floor > bound ? floor : bound;
       s_floor[parity][stream][tid] = top.k[kHist - 1];
     }
-    // Without a posted flag every queue holds at most kQueue - 3 keys here
-    // (a flag is posted at kQueue - 2), so the write stays inside the queue.
+    // A queue whose wave posted no flag held at most kQueue - 4 keys at the
+    // block's start (a flag is posted at kQueue - 3), so with the block's two
+    // pushes the write index stays below kQueue - 2.
     s_queue[nq][qslot] = key;
     nq += key > bound ? 1 : 0;
     if (kScores && writer && ok) scores_out[(myT * H + my_h) * max_pages + j] = v * scale;
