@@ -96,19 +96,20 @@ def algorithmic(w):
                 pre_bytes=pre_bytes, pre_pages=pre_pages)
 
 
-def source_digest(name):
-    """Digest of a kernel source and the header it includes, with comments and
-    whitespace removed: it changes when the code does, not when a comment
-    does."""
+def code_digest(text):
+    """Digest of C++ source text with comments and whitespace removed: it
+    changes when the code does, not when a comment does."""
     import hashlib
     import re
-    csrc = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc")
-    text = ""
-    for f in (name, "common.h"):
-        text += open(os.path.join(csrc, f)).read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     return hashlib.sha256("".join(text.split()).encode()).hexdigest()[:16]
+
+
+def source_digest(name):
+    """code_digest of a kernel source followed by the header it includes."""
+    csrc = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc")
+    return code_digest("".join(open(os.path.join(csrc, f)).read() for f in (name, "common.h")))
 
 
 def measured_traffic(kernel, source):

@@ -1,0 +1,49 @@
+"""Host logic of bench.py, without a GPU: the one-GPU refusal, the algorithmic
+work it divides by (against an independent count from the oracle's row
+positions), and the comment-insensitive source digest that keys the counter
+traffic."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_work_counts():
+    for name in ("mixed_small", "edge_prefill", "multi_token_small"):
+        w = W.make_workload(name, 0)
+        alg = bench.algorithmic(w)
+        # decode: every history page of every request once (page + its
+        # block-table entry), plus each row's query and output per head
+        hist = [max((int(s) - 1) // 128, 0) for s in w.dec_seq_lens]
+        want = sum(hist) * (8704 + 4) + w.n_decode_rows * w.H * (128 + 64)
+        assert alg["dec_bytes"] == want and alg["dec_pages"] == sum(hist)
+        # prefill: 2*128*128 flops per (row, head, history page), the rows'
+        # positions from the oracle
+        if w.Rp:
+            _, pos = oracle.rows_prefill(w.cu_seqlens_q, w.pre_ctx)
+            assert alg["pre_flops"] == int(np.sum(pos // 128)) * w.H * 2 * 128 * 128
+        else:
+            assert alg["pre_flops"] == 0
+
+
+def test_code_digest_ignores_comments_only():
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    d = bench.code_digest(code)
+    assert bench.code_digest("/* a note */ int f(int x)\n{ return x + 1; }") == d
+    assert bench.code_digest(code.replace("+ 1", "+ 2")) != d
+    assert bench.source_digest("prefill.hip") != bench.source_digest("decode.hip")
