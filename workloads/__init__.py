@@ -80,6 +80,9 @@ CONFIGS = {
     "edge_prefill": dict(prefill=dict(ctx=[0, 0, 127, 1, 1919, 5000],
                                       new=[1, 130, 2, 300, 257, 64]), H=3, budget=8),
     "edge_heads5": dict(decode=dict(R=5, lo=1, hi=7000, query_len=5), H=5),
+    # prefill requests with no new rows between others (empty query ranges)
+    "edge_prefill_empty": dict(prefill=dict(ctx=[300, 0, 5000, 77, 2048],
+                                            new=[0, 5, 0, 129, 0]), H=4, budget=0),
     # prefill tiles of 256 rows (one head) and 32 rows (eight heads)
     "prefill_h1_small": dict(prefill=dict(R=2, new=300, ctx_lo=0, ctx_hi=3000), H=1, budget=0),
     "prefill_h8_small": dict(prefill=dict(R=3, new=100, ctx_lo=500, ctx_hi=4000), H=8, budget=0),
