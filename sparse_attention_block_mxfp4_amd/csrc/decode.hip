@@ -4,10 +4,12 @@
 // Plan (one workgroup): history pages of request r are 0..hist_r-1 with
 // hist_r = (seq_len_r - 1) / 128 (the last query's local page bounds every
 // row of the request), clamped to max_pages.  A chunk size is picked so that
-// the whole batch splits into about kTargetItems equal work items (at least
-// kMinChunk pages each); every request gets max(1, ceil(hist_r / chunk_r))
-// items, each one wave's worth of work, with chunk_r = chunk raised where
-// needed so that no request has more than kMaxItemsPerReq items.  Items = (request, first page, end
+// the whole batch splits into at most as many equal work items (at least
+// kMinChunk pages each) as the scorer can hold resident at once -- a second
+// round of items would double the tail; every request gets max(1,
+// ceil(hist_r / chunk_r)) items, each one wave's worth of work, with chunk_r
+// = chunk raised where needed so that no request has more than
+// kMaxItemsPerReq items.  Items = (request, first page, end
 // page); the request's first item and item count go to the workspace.
 //
 // Score (4 independent waves per workgroup, one item each): a wave streams
@@ -18,6 +20,7 @@
 // Merge (one wave per request column, a second launch on the same stream, so
 // the lists written by every XCD are visible without device-wide fences):
 // merges the request's item lists into the 16 output slots of every row.
+#include <atomic>
 #include <cmath>
 
 #include "common.h"
@@ -76,7 +79,7 @@ __device__ __forceinline__ int history_of(const int32_t *seq_lens, int r, int ma
 
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     const int32_t *__restrict__ seq_lens, int num_reqs, int max_pages, int query_len,
-    int capacity, int rows, int32_t *__restrict__ plan, uint8_t *__restrict__ ws) {
+    int capacity, int rows, int resident, int32_t *__restrict__ plan, uint8_t *__restrict__ ws) {
   constexpr int kWaves = kPlanThreads / 64;
   __shared__ long long s_wave[2][kWaves];
   __shared__ long long s_first[kPlanThreads];
@@ -93,7 +96,10 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
   long long total = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) total += s_wave[0][w];
-  const int chunk = (int)max((long long)kMinChunk, (total + kTargetItems - 1) / kTargetItems);
+  // each request rounds its item count up by less than one, so aiming at
+  // resident - num_reqs items keeps the total within what runs at once
+  const long long aim = max((long long)resident / 2, (long long)resident - num_reqs);
+  const int chunk = (int)max((long long)kMinChunk, (total + aim - 1) / aim);
   auto chunk_of = [&](int h) {
     return max(chunk, (h + kMaxItemsPerReq - 1) / kMaxItemsPerReq);
   };
@@ -485,6 +491,52 @@ extern "C" size_t mi_idx_decode_workspace_bytes(int max_reqs, int query_len, int
   return lists_offset(max_reqs) + lists_bytes(decode_capacity(max_reqs), query_len * num_heads);
 }
 
+// Waves of the decode scorer (one item each) that the device holds at once
+// for `rows` query columns, capped at kTargetItems (the plan capacity per
+// batch).  The plan knows neither the query dtype nor whether scores are
+// written, so it takes the lowest occupancy of the four instantiations for
+// the column group count; once per device and count.
+template <int N>
+static hipError_t min_score_blocks(int *blocks) {
+  int b[4] = {0, 0, 0, 0};
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[0], decode_score_kernel<N, false, false>, 256, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[1], decode_score_kernel<N, true, false>, 256, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[2], decode_score_kernel<N, false, true>, 256, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[3], decode_score_kernel<N, true, true>, 256, 0);
+  *blocks = min(min(b[0], b[1]), min(b[2], b[3]));
+  return e;
+}
+
+static int resident_items(int rows) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices][5];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kTargetItems;
+  }
+  const int ncg = min(max((rows + 15) / 16, 1), 4);
+  const int hit = cache[dev][ncg].load(std::memory_order_relaxed);
+  if (hit > 0) return hit;
+  int blocks = 0, cus = 0;
+  hipError_t e = hipSuccess;
+  switch (ncg) {
+    case 1: e = min_score_blocks<1>(&blocks); break;
+    case 2: e = min_score_blocks<2>(&blocks); break;
+    case 3: e = min_score_blocks<3>(&blocks); break;
+    default: e = min_score_blocks<4>(&blocks); break;
+  }
+  if (e != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return kTargetItems;
+  }
+  const long long waves = (long long)blocks * 4 * cus;
+  const int r = waves > 0 ? (int)min(waves, (long long)kTargetItems) : kTargetItems;
+  cache[dev][ncg].store(r, std::memory_order_relaxed);
+  return r;
+}
+
 static int plan_capacity(size_t plan_bytes) {
   if (plan_bytes < (size_t)kPlanHeaderInts * 4) return 0;
   const size_t c = (plan_bytes - kPlanHeaderInts * 4) / (kItemInts * 4);
@@ -521,9 +573,10 @@ extern "C" int mi_idx_plan_decode(const int32_t *seq_lens, int num_reqs, int que
   if (((uintptr_t)plan % 16) || ((uintptr_t)workspace % 16))
     return mi_idx_fail(MI_IDX_EINVAL, "plan_decode: plan and workspace must be 16-byte aligned");
   const int cap = plan_capacity(plan_bytes);
+  const int resident = resident_items(query_len * num_heads);
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, seq_lens,
-                     num_reqs, max_pages, query_len, cap, query_len * num_heads, (int32_t *)plan,
-                     (uint8_t *)workspace);
+                     num_reqs, max_pages, query_len, cap, query_len * num_heads, resident,
+                     (int32_t *)plan, (uint8_t *)workspace);
   return mi_idx_check_launch("plan_decode");
 }
 
