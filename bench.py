@@ -112,20 +112,24 @@ def source_digest(name):
     return code_digest("".join(open(os.path.join(csrc, f)).read() for f in (name, "common.h")))
 
 
-def measured_traffic(kernel, source):
-    """HBM bytes per launch of `kernel` (FETCH_SIZE + WRITE_SIZE, scaled by the
-    copy calibration) from the committed rocprofv3 summary, or None when the
-    kernel's source has changed since the counters were taken."""
+def measured_traffic(kernels, source):
+    """HBM bytes per launch of the named kernels together (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy calibration) from the committed rocprofv3
+    summary, or None when any of them is missing there or its source has
+    changed since the counters were taken."""
     summary = os.path.join(ROOT, "profiles", "mixed_step_kernels.txt")
     src = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc", source)
     if not (os.path.exists(summary) and os.path.exists(src)):
         return None
     digest = source_digest(source)
+    found = {}
     for line in open(summary):
         f = line.split()
-        if len(f) == 4 and f[0] == kernel and f[3] == digest:
-            return int(float(f[1]) + float(f[2]))
-    return None
+        if len(f) == 4 and f[0] in kernels and f[3] == digest:
+            found[f[0]] = float(f[1]) + float(f[2])
+    if set(found) != set(kernels):
+        return None
+    return int(sum(found.values()))
 
 
 def cpu_baseline(w, budget_s):
@@ -391,12 +395,12 @@ def main():
     }
     roof_dec = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
-                "traffic": (measured_traffic("decode_score_kernel", "decode.hip")
+                "traffic": (measured_traffic(("decode_score_kernel", "decode_merge_kernel"), "decode.hip")
                             if w.q_dtype == "e4m3" else None),
                 "kernel": "decode_score_kernel + decode_merge_kernel"}
     roof_pre = {"bound": "mfma", "achieved": round(pre_tflops, 1), "peak": peak_mfma,
                 "unit": "TFLOP/s", "frac": round(pre_tflops / peak_mfma, 4),
-                "traffic": (measured_traffic("prefill_score_kernel", "prefill.hip")
+                "traffic": (measured_traffic(("prefill_score_kernel",), "prefill.hip")
                             if w.q_dtype == "e4m3" else None),
                 "kernel": "prefill_score_kernel"}
     dominant = roof_pre if (w.Rp and pre_ms >= dec_ms) else roof_dec

@@ -47,3 +47,26 @@ def test_code_digest_ignores_comments_only():
     assert bench.code_digest("/* a note */ int f(int x)\n{ return x + 1; }") == d
     assert bench.code_digest(code.replace("+ 1", "+ 2")) != d
     assert bench.source_digest("prefill.hip") != bench.source_digest("decode.hip")
+
+
+def test_measured_traffic_sums_kernels_and_checks_digest(tmp_path, monkeypatch):
+    csrc = tmp_path / "sparse_attention_block_mxfp4_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "k.hip").write_text("__global__ void a() {}\n")
+    (csrc / "common.h").write_text("#pragma once\n")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    d = bench.source_digest("k.hip")
+    (tmp_path / "profiles" / "mixed_step_kernels.txt").write_text(
+        "kernel fetch_bytes write_bytes source_digest\n"
+        f"ka 1000 24 {d}\nkb 300 7 {d}\nkc 5 5 0000000000000000\n")
+    assert bench.measured_traffic(("ka",), "k.hip") == 1024
+    assert bench.measured_traffic(("ka", "kb"), "k.hip") == 1331
+    # a kernel without a line, or with a stale digest, gives no figure
+    assert bench.measured_traffic(("ka", "kz"), "k.hip") is None
+    assert bench.measured_traffic(("kc",), "k.hip") is None
+    # a code change makes every line stale; a comment does not
+    (csrc / "k.hip").write_text("// note\n__global__ void a() {}\n")
+    assert bench.measured_traffic(("ka",), "k.hip") == 1024
+    (csrc / "k.hip").write_text("__global__ void a() { int x; }\n")
+    assert bench.measured_traffic(("ka",), "k.hip") is None
