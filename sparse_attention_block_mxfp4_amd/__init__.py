@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmi_idx.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m sparse_attention_block_mxfp4_amd.build` "
+        f"{LIB_PATH} is not built; run `python sparse_attention_block_mxfp4_amd/build.py` "
         "(or __graft_entry__.build()) with the ROCm toolchain")
 lib = ctypes.CDLL(LIB_PATH)
 
