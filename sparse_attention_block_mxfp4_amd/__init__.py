@@ -39,9 +39,11 @@ _SIGS = {
     "mi_idx_score_topk_decode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
                                         _i32, _f32, _vp, _sz, _vp, _sz, _vp, _vp, _vp]),
     "mi_idx_prefill_plan_bytes": (_sz, [_i32, _i64, _i32]),
-    "mi_idx_plan_prefill": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp, _vp, _vp]),
+    "mi_idx_prefill_workspace_bytes": (_sz, []),
+    "mi_idx_plan_prefill": (_i32, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _sz, _vp, _vp]),
     "mi_idx_score_topk_prefill": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32,
-                                         _i64, _i32, _i32, _f32, _vp, _sz, _i32, _vp, _vp, _vp]),
+                                         _i64, _i32, _i32, _f32, _vp, _sz, _vp, _vp, _sz, _vp,
+                                         _vp, _vp]),
     "mi_idx_select_forced": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
     "mi_idx_norm_rope_insert_mxfp4": (_i32, [_vp, _i32, _i64, _vp, _f32, _vp, _i32, _c.c_double,
                                              _i32, _vp, _i64, _vp, _i64, _vp]),
@@ -223,11 +225,21 @@ def mi_idx_prefill_plan_bytes(num_reqs, total_q, num_heads):
     return int(lib.mi_idx_prefill_plan_bytes(num_reqs, total_q, num_heads))
 
 
+class PrefillLaunch(ctypes.Structure):
+    """mi_idx_prefill_launch: the launch shape of a prefill plan."""
+    _fields_ = [("num_lists", ctypes.c_int32), ("num_pieces", ctypes.c_int32),
+                ("num_merges", ctypes.c_int32), ("num_chunks", ctypes.c_int32)]
+
+
+def mi_idx_prefill_workspace_bytes():
+    return int(lib.mi_idx_prefill_workspace_bytes())
+
+
 def mi_idx_plan_prefill(cu_seqlens_q_host, seq_lens_host, num_heads, gather_budget_pages,
                         staging, plan, stream=None):
-    """Host plan of the prefill tiles; one async copy of ``staging`` (pinned
-    host uint8 tensor) into ``plan`` (device uint8 tensor).  Returns
-    (num_tiles, num_chunks)."""
+    """Host plan of the prefill work lists; one async copy of ``staging``
+    (pinned host uint8 tensor) into ``plan`` (device uint8 tensor).  Returns
+    the plan's PrefillLaunch (work lists, pieces, split tiles, chunks)."""
     cu = np.ascontiguousarray(np.asarray(cu_seqlens_q_host, dtype=np.int32))
     sl = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
     if cu.ndim != 1 or sl.ndim != 1 or cu.size != sl.size + 1:
@@ -238,21 +250,21 @@ def mi_idx_plan_prefill(cu_seqlens_q_host, seq_lens_host, num_heads, gather_budg
     _need(plan, "plan", _U8)
     if staging.numel() < plan.numel():
         raise ValueError("staging must be at least as large as plan")
-    tiles = ctypes.c_int(0)
-    chunks = ctypes.c_int(0)
+    launch = PrefillLaunch()
     st = lib.mi_idx_plan_prefill(cu.ctypes.data, sl.ctypes.data, sl.size, num_heads,
                                  int(gather_budget_pages), _ptr(staging), _ptr(plan),
-                                 plan.numel(), ctypes.byref(chunks), ctypes.byref(tiles),
-                                 _stream(stream))
+                                 plan.numel(), ctypes.byref(launch), _stream(stream))
     _check(st, "mi_idx_plan_prefill")
-    return tiles.value, chunks.value
+    return launch
 
 
 def mi_idx_score_topk_prefill(q, pages, block_table, cu_seqlens_q, seq_lens, context_lens,
-                              max_pages, plan, num_tiles, topk_out, scale=1.0, scores_out=None,
-                              stream=None):
+                              max_pages, plan, launch, workspace, topk_out, scale=1.0,
+                              scores_out=None, stream=None):
     """q [total_q, H, 128] E4M3 or bfloat16; topk_out [total_q, H, 16] int32
-    (may be a row slice of a larger contiguous buffer)."""
+    (may be a row slice of a larger contiguous buffer); launch: the
+    PrefillLaunch of the plan; workspace: device uint8 tensor of
+    mi_idx_prefill_workspace_bytes() (None when launch.num_merges is 0)."""
     _need(q, "q", _QALL)
     _need(pages, "pages", _U8)
     _need(block_table, "block_table", _I32, contiguous=False)
@@ -274,10 +286,13 @@ def mi_idx_score_topk_prefill(q, pages, block_table, cu_seqlens_q, seq_lens, con
         _need(scores_out, "scores_out", (torch.float32,))
         if tuple(scores_out.shape) != (T, H, max_pages):
             raise ValueError("scores_out must be [total_q, H, max_pages]")
+    if workspace is not None:
+        _need(workspace, "workspace", _U8)
     st = lib.mi_idx_score_topk_prefill(
         _ptr(q), _q_dtype(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
         block_table.stride(0), _ptr(cu_seqlens_q), _ptr(seq_lens), _ptr(context_lens), R, T, H,
-        max_pages, float(scale), _ptr(plan), plan.numel(), num_tiles, _ptr(topk_out),
+        max_pages, float(scale), _ptr(plan), plan.numel(), ctypes.byref(launch),
+        _ptr(workspace), workspace.numel() if workspace is not None else 0, _ptr(topk_out),
         _ptr(scores_out), _stream(stream))
     _check(st, "mi_idx_score_topk_prefill")
 

@@ -5,9 +5,10 @@ The split mirrors the vllm pages (``indexer_nvfp4`` MiniMaxM3IndexerNvfp4Impl
 .forward and ``indexer_mxfp4`` MiniMaxM3IndexerRocmMxfp4Impl.forward: decode
 rows occupy the first rows of the shared buffer, prefill rows follow; the
 plans are built once per step, the scorers run once per layer).  The persistent
-buffers (decode plan and workspace, prefill plan, pinned staging) are
-allocated once for the maxima given to the constructor and refilled in place
-every step, so a captured decode phase keeps valid addresses.
+buffers (decode plan and workspace, prefill plan, workspace and pinned
+staging) are allocated once for the maxima given to the constructor and
+refilled in place every step, so a captured decode phase keeps valid
+addresses.
 
 Every call goes through the C ABI (``mi_idx_*``); this class only owns the
 buffers.
@@ -21,6 +22,7 @@ from . import (
     mi_idx_plan_decode,
     mi_idx_plan_prefill,
     mi_idx_prefill_plan_bytes,
+    mi_idx_prefill_workspace_bytes,
     mi_idx_score_topk_decode,
     mi_idx_score_topk_prefill,
 )
@@ -40,15 +42,16 @@ class IndexerStep:
             self.dec_ws = torch.empty(
                 mi_idx_decode_workspace_bytes(max_decode_reqs, self.query_len, self.H),
                 dtype=torch.uint8, device=self.device)
-        self.pre_plan = None
+        self.pre_plan = self.pre_ws = None
         self.pre_staging = []
         self._staging_done = []
         self._next_staging = 0
-        self.num_tiles = 0
-        self.num_chunks = 0
+        self.pre_launch = None
         if max_prefill_reqs > 0:
             nb = mi_idx_prefill_plan_bytes(max_prefill_reqs, max_prefill_rows, self.H)
             self.pre_plan = torch.empty(nb, dtype=torch.uint8, device=self.device)
+            self.pre_ws = torch.empty(mi_idx_prefill_workspace_bytes(), dtype=torch.uint8,
+                                      device=self.device)
             # Two pinned staging buffers used in turn: a buffer is rewritten
             # only after the copy that last read it has completed.
             self.pre_staging = [torch.empty(nb, dtype=torch.uint8, pin_memory=True)
@@ -61,13 +64,13 @@ class IndexerStep:
         if decode_seq_lens is not None and decode_seq_lens.numel() > 0:
             mi_idx_plan_decode(decode_seq_lens, self.query_len, self.H, self.max_pages,
                                self.dec_plan, self.dec_ws, stream=stream)
-        self.num_tiles = 0
+        self.pre_launch = None
         if prefill_cu_seqlens_q_host is not None and len(prefill_seq_lens_host) > 0:
             k = self._next_staging
             self._next_staging ^= 1
             if self._staging_done[k] is not None:
                 self._staging_done[k].synchronize()
-            self.num_tiles, self.num_chunks = mi_idx_plan_prefill(
+            self.pre_launch = mi_idx_plan_prefill(
                 prefill_cu_seqlens_q_host, prefill_seq_lens_host, self.H, gather_budget_pages,
                 self.pre_staging[k], self.pre_plan, stream=stream)
             ev = torch.cuda.Event()
@@ -82,8 +85,8 @@ class IndexerStep:
 
     def prefill(self, q, pages, block_table, cu_seqlens_q, seq_lens, context_lens, out,
                 scale=1.0, scores_out=None, stream=None):
-        if self.num_tiles == 0:
+        if self.pre_launch is None or self.pre_launch.num_lists == 0:
             return
         mi_idx_score_topk_prefill(q, pages, block_table, cu_seqlens_q, seq_lens, context_lens,
-                                  self.max_pages, self.pre_plan, self.num_tiles, out,
-                                  scale=scale, scores_out=scores_out, stream=stream)
+                                  self.max_pages, self.pre_plan, self.pre_launch, self.pre_ws,
+                                  out, scale=scale, scores_out=scores_out, stream=stream)

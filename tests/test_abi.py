@@ -30,7 +30,7 @@ def m():
 
 def test_library_exports_every_declared_symbol(m):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     raw = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -52,8 +52,12 @@ def test_sizes(m):
     assert m.mi_idx_decode_plan_bytes(64) == 64 + (64 + 2048) * 16
     assert m.mi_idx_decode_workspace_bytes(64, 1, 1) == 256 + 512 + (64 + 2048) * 16 * 8
     assert m.mi_idx_decode_workspace_bytes(0, 0, 1) == 0
-    assert m.mi_idx_prefill_plan_bytes(8, 32768, 4) == 64 + (32768 // 64 + 8 + 1) * 16
+    # header, 512 work lists, tiles + 512 pieces, 512 split tiles
+    tiles = 32768 // 64 + 8 + 1
+    assert m.mi_idx_prefill_plan_bytes(8, 32768, 4) == 4 * (16 + 4 * 512 + 8 * (tiles + 512)
+                                                            + 8 * 512)
     assert m.mi_idx_prefill_plan_bytes(1, 10, 9) == 0
+    assert m.mi_idx_prefill_workspace_bytes() == 1024 * 256 * 16 * 8
 
 
 def _fake(n=1 << 20):
@@ -170,10 +174,13 @@ def test_prefill_argument_errors(m):
     L = m.lib
     buf = _fake().ctypes.data
     pb = m.mi_idx_prefill_plan_bytes(2, 100, 1)
-    args = [buf, 0, buf, 10, buf, 16, buf, buf, buf, 2, 100, 1, 16, 1.0, buf, pb, 2, buf, None,
-            None]
+    wb = m.mi_idx_prefill_workspace_bytes()
+    launch = m.PrefillLaunch(2, 3, 1, 1)
+    args = [buf, 0, buf, 10, buf, 16, buf, buf, buf, 2, 100, 1, 16, 1.0, buf, pb,
+            ctypes.addressof(launch), buf, wb, buf, None, None]
 
-    def call(i=None, v=None):
+    def call(i=None, v=None, shape=(2, 3, 1, 1)):
+        launch.num_lists, launch.num_pieces, launch.num_merges, launch.num_chunks = shape
         a = list(args)
         if i is not None:
             a[i] = v
@@ -181,22 +188,101 @@ def test_prefill_argument_errors(m):
     assert call(11, 9) == m.EUNSUPPORTED
     assert call(13, -1.0) == m.EINVAL
     assert call(0, None) == m.EINVAL
-    assert call(16, 10 ** 6) == m.ECAPACITY
+    assert call(16, None) == m.EINVAL            # no launch shape
+    assert call(shape=(10 ** 6, 10 ** 6, 0, 1)) == m.ECAPACITY
+    assert call(shape=(2, 3, 10 ** 6, 1)) == m.ECAPACITY   # more split tiles than work lists
+    assert call(shape=(2, 3, -1, 1)) == m.EINVAL
+    assert call(shape=(3, 2, 0, 1)) == m.EINVAL  # fewer pieces than work lists
+    assert call(17, None) == m.EINVAL            # split tiles need the workspace
+    assert call(17, buf + 4) == m.EINVAL         # misaligned workspace
+    assert call(18, wb - 1) == m.ECAPACITY
     assert call(5, 8) == m.EINVAL
     assert call(1, 5) == m.EINVAL               # unknown q dtype
-    assert call(16, 0) == m.OK
+    assert call(shape=(0, 0, 0, 0)) == m.OK
     cu = np.array([0, 5, 3], dtype=np.int32)
     sl = np.array([10, 10], dtype=np.int32)
-    tiles, ch = ctypes.c_int(), ctypes.c_int()
+    out = m.PrefillLaunch()
     st = _fake()
-    assert L.mi_idx_plan_prefill(cu.ctypes.data, sl.ctypes.data, 2, 1, 0, st.ctypes.data, buf,
-                                 pb, ctypes.byref(ch), ctypes.byref(tiles), None) == m.EINVAL
+
+    def plan(nbytes=pb, shape=ctypes.byref(out)):
+        return L.mi_idx_plan_prefill(cu.ctypes.data, sl.ctypes.data, 2, 1, 0, st.ctypes.data, buf,
+                                     nbytes, shape, None)
+    assert plan() == m.EINVAL
     cu = np.array([0, 5, 30], dtype=np.int32)
-    assert L.mi_idx_plan_prefill(cu.ctypes.data, sl.ctypes.data, 2, 1, 0, st.ctypes.data, buf,
-                                 pb, ctypes.byref(ch), ctypes.byref(tiles), None) == m.EINVAL
+    assert plan() == m.EINVAL
     cu = np.array([0, 5, 8], dtype=np.int32)
-    assert L.mi_idx_plan_prefill(cu.ctypes.data, sl.ctypes.data, 2, 1, 0, st.ctypes.data, buf,
-                                 16, ctypes.byref(ch), ctypes.byref(tiles), None) == m.ECAPACITY
+    assert plan(nbytes=16) == m.ECAPACITY
+    assert plan(shape=None) == m.EINVAL
+
+
+def _plan_host(m, cu, sl, H, budget):
+    """Run the host plan; return the staging words it wrote and its outputs."""
+    R = len(sl)
+    pb = m.mi_idx_prefill_plan_bytes(R, int(cu[-1]), H)
+    st = _fake(pb)
+    out = m.PrefillLaunch()
+    status = m.lib.mi_idx_plan_prefill(cu.ctypes.data, sl.ctypes.data, R, H, budget,
+                                       st.ctypes.data, 256, pb, ctypes.byref(out), None)
+    # no device here: the single copy fails after the staging is written
+    assert status in (m.OK, m.EHIP)
+    words = st.view(np.int32)
+    assert out.num_pieces == words[4]
+    return words, out.num_lists, out.num_chunks, out.num_merges
+
+
+def _check_plan(words, n_lists, n_chunks, n_merges, cu, sl, H, budget):
+    """Every row in exactly one tile of M rows; each tile's pieces split its
+    pages [0, pages) into consecutive ranges; split tiles carry consecutive
+    slots and one merge record; work lists hold consecutive pieces; chunks
+    follow in order.  Returns the list costs (pages + 32 per piece)."""
+    R = len(sl)
+    qn = np.diff(cu)
+    M = 256 // H
+    assert words[0] == n_lists and words[1] == M and words[2] == H and words[3] == n_chunks
+    n_pieces, poff, n_split, soff, n_slots = (int(x) for x in words[4:9])
+    assert n_split == n_merges
+    assert 1 <= n_lists <= 256 or (n_lists == 0 and n_pieces == 0)
+    lists = words[16:16 + 4 * n_lists].reshape(-1, 4)
+    assert poff == 16 + 4 * n_lists and soff == poff + 8 * n_pieces
+    # the lists, in piece order, cover the pieces once, consecutively
+    nxt = 0
+    for first, cnt, _, _ in sorted(lists.tolist()):
+        assert first == nxt and cnt >= 1
+        nxt += cnt
+    assert nxt == n_pieces
+    pieces = words[poff:poff + 8 * n_pieces].reshape(-1, 8)
+    splits = words[soff:soff + 8 * n_split].reshape(-1, 8)
+    want_chunks = oracle.prefill_chunks(sl, budget if budget > 0 else 10 ** 12)
+    assert n_chunks == len(want_chunks)
+    chunk_of = np.zeros(R, dtype=int)
+    for c, (a, b, _) in enumerate(want_chunks):
+        chunk_of[a:b] = c
+    cover = [np.zeros(q, dtype=int) for q in qn]
+    ranges = {}
+    for r, row0, nr, pa, pe, slot, _, _ in pieces:
+        assert 0 < nr <= M and row0 % M == 0
+        ranges.setdefault((r, row0, nr), []).append((pa, pe, slot))
+    for (r, row0, nr), rs in ranges.items():
+        cover[r][row0:row0 + nr] += 1
+        pages = max((sl[r] - qn[r] + row0 + nr - 1) // 128, 0)
+        assert rs[0][0] == 0 and rs[-1][1] == pages
+        for (a0, b0, _), (a1, _, _) in zip(rs, rs[1:]):
+            assert b0 == a1 and a0 < b0
+        slots = [x[2] for x in rs]
+        if len(rs) == 1:
+            assert slots == [-1]
+        else:
+            assert slots == list(range(slots[0], slots[0] + len(rs)))
+            match = [s for s in splits if tuple(s[:3]) == (r, row0, nr)]
+            assert len(match) == 1 and match[0][3] == slots[0] and match[0][4] == len(rs)
+    assert all(np.all(c == 1) for c in cover)
+    assert len(splits) == sum(1 for rs in ranges.values() if len(rs) > 1)
+    assert n_slots == sum(len(rs) for rs in ranges.values() if len(rs) > 1)
+    # chunks are launched in order (the tile order inside a chunk is a
+    # placement choice and is not part of the contract)
+    ch_seq = [chunk_of[p[0]] for p in pieces]
+    assert ch_seq == sorted(ch_seq)
+    return [int(sum(p[4] - p[3] + 32 for p in pieces[f:f + c])) for f, c, _, _ in lists]
 
 
 @pytest.mark.parametrize("H", [1, 3, 4, 8])
@@ -210,33 +296,35 @@ def test_prefill_host_plan_matches_oracle_chunking(m, H):
         sl = np.maximum(sl, 1).astype(np.int32)
         cu = np.concatenate([[0], np.cumsum(qn)]).astype(np.int32)
         budget = int(rng.integers(0, 60))
-        pb = m.mi_idx_prefill_plan_bytes(R, int(cu[-1]), H)
-        st = _fake(pb)
-        tiles, ch = ctypes.c_int(), ctypes.c_int()
-        status = m.lib.mi_idx_plan_prefill(cu.ctypes.data, sl.ctypes.data, R, H, budget,
-                                           st.ctypes.data, 256, pb, ctypes.byref(ch),
-                                           ctypes.byref(tiles), None)
-        # no device here: the single copy fails after the staging is written
-        assert status in (m.OK, m.EHIP)
-        words = st.view(np.int32)
-        n = words[0]
-        assert n == tiles.value
-        M = 256 // H
-        assert words[1] == M and words[2] == H
-        want_chunks = oracle.prefill_chunks(sl, budget if budget > 0 else 10 ** 12)
-        assert words[3] == len(want_chunks) == ch.value
-        t = words[16:16 + 4 * n].reshape(n, 4)
-        chunk_of = np.zeros(R, dtype=int)
-        for c, (a, b, _) in enumerate(want_chunks):
-            chunk_of[a:b] = c
-        # tiles cover every row exactly once, in row tiles of M
-        cover = [np.zeros(q, dtype=int) for q in qn]
-        for r, row0, nr, pages in t:
-            assert 0 < nr <= M and row0 % M == 0
-            cover[r][row0:row0 + nr] += 1
-            assert pages == max((sl[r] - qn[r] + row0 + nr - 1) // 128, 0)
-        assert all(np.all(c == 1) for c in cover)
-        # chunks are launched in order (the tile order inside a chunk is a
-        # placement choice and is not part of the contract)
-        ch_seq = [chunk_of[r] for r, _, _, _ in t]
-        assert ch_seq == sorted(ch_seq)
+        words, n, ch, mg = _plan_host(m, cu, sl, H, budget)
+        _check_plan(words, n, ch, mg, cu, sl, H, budget)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefill_work_lists_balance_ragged_rows(m, seed):
+    """Ragged prefill shapes (8 requests x 4096 rows over 0..61440 context
+    tokens, 4 heads): at most 256 lists (one per CU without a device), none
+    costing more than 1.35 x the balanced share or the longest tile."""
+    rng = np.random.default_rng(seed)
+    qn = np.full(8, 4096, dtype=np.int32)
+    ctx = rng.integers(0, 61441, size=8).astype(np.int32)
+    sl = (ctx + qn).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(qn)]).astype(np.int32)
+    words, n, ch, mg = _plan_host(m, cu, sl, 4, 1024)
+    costs = _check_plan(words, n, ch, mg, cu, sl, 4, 1024)
+    M = 64
+    tile_cost = [max((c + r0 + M - 1) // 128, 0) + 32 for c in ctx for r0 in range(0, 4096, M)]
+    share = sum(tile_cost) / 256
+    assert n <= 256 and max(costs) <= 1.35 * share
+    assert mg > 0                       # the longest tiles exceed the share and are split
+
+
+def test_prefill_equal_tiles_stay_whole(m):
+    """Two requests of 8192 rows over 131072-token contexts (tiles within 5 %
+    of each other): one whole tile per list, nothing to merge."""
+    qn = np.full(2, 8192, dtype=np.int32)
+    sl = (131072 + qn).astype(np.int32)
+    cu = np.concatenate([[0], np.cumsum(qn)]).astype(np.int32)
+    words, n, ch, mg = _plan_host(m, cu, sl, 4, 0)
+    _check_plan(words, n, ch, mg, cu, sl, 4, 0)
+    assert n == 256 and mg == 0

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 SMALL = ["tiny_decode", "decode_batch_small", "multi_token_small", "ragged_prefill_small",
          "mixed_small", "edge_short", "edge_wide", "edge_prefill", "edge_prefill_empty",
          "edge_heads5",
-         "prefill_h1_small", "prefill_h8_small"]
+         "prefill_h1_small", "prefill_h8_small", "prefill_many_tiles"]
 
 
 def _banner(msg):

@@ -86,6 +86,10 @@ CONFIGS = {
     # prefill tiles of 256 rows (one head) and 32 rows (eight heads)
     "prefill_h1_small": dict(prefill=dict(R=2, new=300, ctx_lo=0, ctx_hi=3000), H=1, budget=0),
     "prefill_h8_small": dict(prefill=dict(R=3, new=100, ctx_lo=500, ctx_hi=4000), H=8, budget=0),
+    # more row tiles (300) than the device has workgroups: work lists of
+    # several pieces, whole tiles and page ranges of split tiles mixed
+    "prefill_many_tiles": dict(prefill=dict(R=6, new=3200, ctx_lo=0, ctx_hi=2000), H=4,
+                               budget=0),
     # monotone-score cases (tests give them constructed K and Q; see
     # tests/test_gpu_trends.py): long histories in which every page is, or
     # no page after the first 15 is, a new top-15 entry
