@@ -112,12 +112,13 @@ def source_digest(name):
     return code_digest("".join(open(os.path.join(csrc, f)).read() for f in (name, "common.h")))
 
 
-def measured_traffic(kernels, source):
+def measured_traffic(kernels, source, workload="mixed_step"):
     """HBM bytes per launch of the named kernels together (FETCH_SIZE +
     WRITE_SIZE, scaled by the copy calibration) from the committed rocprofv3
-    summary, or None when any of them is missing there or its source has
-    changed since the counters were taken."""
-    summary = os.path.join(ROOT, "profiles", "mixed_step_kernels.txt")
+    summary of the same workload, or None when there is none, when any of
+    the kernels is missing there or when its source has changed since the
+    counters were taken."""
+    summary = os.path.join(ROOT, "profiles", f"{workload}_kernels.txt")
     src = os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "csrc", source)
     if not (os.path.exists(summary) and os.path.exists(src)):
         return None
@@ -208,24 +209,28 @@ def _cpu_model():
 
 KERNEL_SOURCES = {"decode_plan_kernel": "decode.hip", "decode_score_kernel": "decode.hip",
                   "decode_merge_kernel": "decode.hip", "prefill_score_kernel": "prefill.hip",
-                  "insert_kernel": "insert.hip"}
-PROFILE_COMMANDS = [
-    ("kernel trace + stats (the bench's own timed configuration)",
-     "rocprofv3 --kernel-trace --stats -T -f csv -d DIR/prof_trace -o trace"
-     " -- python bench.py --no-cpu-baseline"),
-    ("FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_fetch -o fetch"
-     " -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
-    ("WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_write -o write"
-     " -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
-    ("copy calibration, FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_copyf -o copyf"
-     " -- python bench.py --copy-calibration"),
-    ("copy calibration, WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_copyw -o copyw"
-     " -- python bench.py --copy-calibration"),
-    ("SQ counters", "rocprofv3 --pmc SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS "
-     "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE -T -f csv "
-     "-d DIR/prof_sq -o sq -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline"),
-    ("summary", "python bench.py --summarize-profiles DIR"),
-]
+                  "prefill_merge_kernel": "prefill.hip", "insert_kernel": "insert.hip"}
+def profile_commands(workload):
+    """The rocprofv3 runs behind profiles/<workload>_kernels.txt (W = the
+    workload option, empty for the default mixed step)."""
+    W = "" if workload == "mixed_step" else f" --workload {workload}"
+    return [
+        ("kernel trace + stats (the bench's own timed configuration)",
+         "rocprofv3 --kernel-trace --stats -T -f csv -d DIR/prof_trace -o trace"
+         f" -- python bench.py --no-cpu-baseline{W}"),
+        ("FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_fetch -o fetch"
+         f" -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline{W}"),
+        ("WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_write -o write"
+         f" -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline{W}"),
+        ("copy calibration, FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_copyf"
+         " -o copyf -- python bench.py --copy-calibration"),
+        ("copy calibration, WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_copyw"
+         " -o copyw -- python bench.py --copy-calibration"),
+        ("SQ counters", "rocprofv3 --pmc SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS "
+         "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE -T -f csv "
+         f"-d DIR/prof_sq -o sq -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline{W}"),
+        ("summary", f"python bench.py --summarize-profiles DIR{W}"),
+    ]
 
 
 def summarize_profiles(d, workload):
@@ -258,7 +263,7 @@ def summarize_profiles(d, workload):
     w_factor = gib / (copy_w * 1024)
     out = [f"# rocprofv3 summary: {workload} workload (bench.py defaults), one MI355X",
            "#", "# commands (run from the repository root; DIR = the output folder):"]
-    for what, cmd in PROFILE_COMMANDS:
+    for what, cmd in profile_commands(workload):
         out.append(f"#   {what}: {cmd}")
     out.append(f"# copy calibration: a plain 1 GiB device copy reads FETCH_SIZE {copy_f:.1f} KiB "
                f"(factor {f_factor:.4f}) and WRITE_SIZE {copy_w:.1f} KiB (factor {w_factor:.4f}) "
@@ -272,7 +277,7 @@ def summarize_profiles(d, workload):
     out += ["", "## HBM traffic per launch (counter KiB x 1024 x calibration factor)",
             "%-24s %16s %16s %s" % ("kernel", "fetch_bytes", "write_bytes", "source_digest")]
     for k in ["decode_plan_kernel", "decode_score_kernel", "decode_merge_kernel",
-              "prefill_score_kernel"]:
+              "prefill_score_kernel", "prefill_merge_kernel"]:
         fv, wv = per_kernel(fetch, k, "FETCH_SIZE"), per_kernel(write, k, "WRITE_SIZE")
         if fv is None or wv is None:
             continue
@@ -283,7 +288,8 @@ def summarize_profiles(d, workload):
         sq = counters(sq_path)
         out += ["", "## SQ counters per launch (GRBM_GUI_ACTIVE is summed over the 8 XCDs; "
                 "MFMA busy is summed over the 1024 SIMDs)"]
-        for k in ["prefill_score_kernel", "decode_score_kernel", "decode_merge_kernel"]:
+        for k in ["prefill_score_kernel", "prefill_merge_kernel", "decode_score_kernel",
+                  "decode_merge_kernel"]:
             g = per_kernel(sq, k, "GRBM_GUI_ACTIVE")
             if g is None:
                 continue
@@ -395,14 +401,19 @@ def main():
     }
     roof_dec = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
-                "traffic": (measured_traffic(("decode_score_kernel", "decode_merge_kernel"), "decode.hip")
+                "traffic": (measured_traffic(("decode_score_kernel", "decode_merge_kernel"),
+                                             "decode.hip", a.workload)
                             if w.q_dtype == "e4m3" else None),
                 "kernel": "decode_score_kernel + decode_merge_kernel"}
+    # the prefill phase is the scorer and, when the plan split tiles, the merge
+    pre_kernels = ("prefill_score_kernel",) + (
+        ("prefill_merge_kernel",) if step.pre_launch is not None and step.pre_launch.num_merges
+        else ())
     roof_pre = {"bound": "mfma", "achieved": round(pre_tflops, 1), "peak": peak_mfma,
                 "unit": "TFLOP/s", "frac": round(pre_tflops / peak_mfma, 4),
-                "traffic": (measured_traffic(("prefill_score_kernel",), "prefill.hip")
+                "traffic": (measured_traffic(pre_kernels, "prefill.hip", a.workload)
                             if w.q_dtype == "e4m3" else None),
-                "kernel": "prefill_score_kernel"}
+                "kernel": " + ".join(pre_kernels)}
     dominant = roof_pre if (w.Rp and pre_ms >= dec_ms) else roof_dec
     res = {
         "metric": METRIC,

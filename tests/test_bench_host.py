@@ -65,6 +65,10 @@ def test_measured_traffic_sums_kernels_and_checks_digest(tmp_path, monkeypatch):
     # a kernel without a line, or with a stale digest, gives no figure
     assert bench.measured_traffic(("ka", "kz"), "k.hip") is None
     assert bench.measured_traffic(("kc",), "k.hip") is None
+    # the summary of another workload is not used
+    assert bench.measured_traffic(("ka",), "k.hip", "ragged_prefill") is None
+    (tmp_path / "profiles" / "ragged_prefill_kernels.txt").write_text(f"ka 7 1 {d}\n")
+    assert bench.measured_traffic(("ka",), "k.hip", "ragged_prefill") == 8
     # a code change makes every line stale; a comment does not
     (csrc / "k.hip").write_text("// note\n__global__ void a() {}\n")
     assert bench.measured_traffic(("ka",), "k.hip") == 1024
