@@ -5,9 +5,9 @@ One step = one pass of the whole hot path over the mixed-step workload
 chunks of 8192 rows over 131072-token histories, 4 index heads): the decode
 plan (device kernel), the decode scorer, the prefill plan (host tiles + one
 pinned H2D copy) and the prefill scorer, all writing one [16448, 4, 16] int32
-buffer.  Inputs are resident in HBM before the timed region.  The decode phase
-reads two pool copies in turn so the 0.5 GB of pages are not served from the
-256 MB Infinity Cache.
+buffer.  Inputs are resident in HBM before the timed region.  The steps read
+pool copies in turn (two for the mixed step's 0.5 GB of pages, more for
+smaller pools) so that pages are not served from the 256 MB Infinity Cache.
 
 Prints ONE JSON line.  Kernel times come from HIP events recorded on the
 stream the kernels run on, inside the timed steps.  The CPU baseline is the
@@ -40,7 +40,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="mixed_step")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--pool-copies", type=int, default=2)
+    p.add_argument("--pool-copies", type=int, default=None,
+                   help="pool copies read in turn (default: enough that two Infinity Caches' "
+                        "worth of other copies is read between two uses of one, 2..16)")
     p.add_argument("--q-dtype", choices=["e4m3", "bf16"], default="e4m3",
                    help="index-Q dtype (E4M3 is the configured workload; bf16 runs the "
                         "bf16-MFMA path)")
@@ -94,6 +96,17 @@ def algorithmic(w):
     pre_bytes = pre_pages * 8704 + w.n_prefill_rows * w.H * (qb + 64)
     return dict(dec_bytes=dec_bytes, dec_pages=dec_pages, pre_flops=pre_flops,
                 pre_bytes=pre_bytes, pre_pages=pre_pages)
+
+
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def auto_pool_copies(pool_bytes):
+    """Copies read in turn so that between two uses of one copy the others
+    move at least twice the Infinity Cache: 1 + ceil(2 * 256 MB / pool),
+    within 2..16."""
+    need = 1 + -(-2 * INFINITY_CACHE_BYTES // max(int(pool_bytes), 1))
+    return int(min(max(need, 2), 16))
 
 
 def code_digest(text):
@@ -334,6 +347,8 @@ def main():
 
     torch.cuda.set_device(0)
     w = W.make_workload(a.workload, a.seed, q_dtype=a.q_dtype)
+    if a.pool_copies is None:
+        a.pool_copies = auto_pool_copies(w.num_blocks * 8704)
     print(f"[bench] staging {a.workload}: T={w.T} H={w.H} pages={w.num_blocks} "
           f"x{a.pool_copies} copies", file=sys.stderr, flush=True)
     dw = DeviceWorkload(w, m.mi_idx_insert_mxfp4, pool_copies=a.pool_copies)

@@ -74,3 +74,12 @@ def test_measured_traffic_sums_kernels_and_checks_digest(tmp_path, monkeypatch):
     assert bench.measured_traffic(("ka",), "k.hip") == 1024
     (csrc / "k.hip").write_text("__global__ void a() { int x; }\n")
     assert bench.measured_traffic(("ka",), "k.hip") is None
+
+
+def test_auto_pool_copies_defeat_the_infinity_cache():
+    mb = 1 << 20
+    assert bench.auto_pool_copies(522 * mb) == 2          # mixed step
+    assert bench.auto_pool_copies(856 * mb) == 2          # multi-token decode
+    n = bench.auto_pool_copies(89 * mb)                   # decode batch
+    assert n == 7 and (n - 1) * 89 * mb >= 2 * 256 * mb
+    assert bench.auto_pool_copies(200 * 1024) == 16       # tiny pools: capped
