@@ -429,30 +429,44 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       // stages after its first page.
       auto block = [&](int k, int rb, int parity, int bt_use, int &bt_next) {
         auto stage = [&]() {
+          __builtin_amdgcn_s_setprio(1);
           pf_commit(rb ^ 2, e0, e1, e2);
           pf_commit((rb ^ 2) + 1, o0, o1, o2);
           bt_next = bt_fetch(k + 6);
           pf_issue(k + 4, __builtin_amdgcn_readlane(bt_use, 0), e0, e1, e2);
           pf_issue(k + 5, __builtin_amdgcn_readlane(bt_use, 1), o0, o1, o2);
+          __builtin_amdgcn_s_setprio(0);
         };
+        // A wave issuing its MFMA chain, or staging the next pages, runs at
+        // raised priority, so that the SIMD's other wave (in its selection
+        // step) does not delay the next MFMA or load (about 1.7 % faster on
+        // the mixed step in A/B).
         maybe_drain(parity);
         if (stream == 0) {
+          __builtin_amdgcn_s_setprio(1);
           page_fold(rb, ma);
+          __builtin_amdgcn_s_setprio(0);
           pin(ma);
           take(page_reduce(mb), k - 1, parity);
           stage();
+          __builtin_amdgcn_s_setprio(1);
           page_fold(rb + 1, mb);
+          __builtin_amdgcn_s_setprio(0);
           pin(mb);
           take(page_reduce(ma), k, parity);
         } else {
           take(page_reduce(mb), k - 1, parity);
           pin(mb);
           stage();
+          __builtin_amdgcn_s_setprio(1);
           page_fold(rb, ma);
+          __builtin_amdgcn_s_setprio(0);
           pin(ma);
           take(page_reduce(ma), k, parity);
           pin(ma);
+          __builtin_amdgcn_s_setprio(1);
           page_fold(rb + 1, mb);
+          __builtin_amdgcn_s_setprio(0);
           pin(mb);
         }
         post(parity);
