@@ -121,6 +121,25 @@ def test_prefill_plan_upper_bounds_and_budget_do_not_matter():
     assert np.array_equal(a, b) and np.array_equal(a, c) and np.array_equal(a, d)
 
 
+def test_prefill_work_lists_repeat_and_upper_bounds():
+    """Multi-piece work lists with split tiles: one plan scored three times
+    (each call rewrites the workspace's partial lists before the merge reads
+    them) and a plan from upper-bound lengths (more splits; pieces past a
+    tile's device pages walk nothing) give the first result, which matches
+    the oracle."""
+    _banner("prefill work lists: repeat, upper bounds")
+    w = W.make_workload("prefill_many_tiles", 1)
+    a, _, _, dw, step = run_gpu(w)
+    sh = step.pre_launch
+    assert sh.num_merges > 0 and sh.num_pieces > sh.num_lists
+    b, _, _, _, _ = run_gpu(w, dw=dw, layers=3)
+    c, _, _, _, step_c = run_gpu(w, dw=dw, seq_lens_host_ub=w.seq_lens[w.Rd:] + 3000)
+    assert step_c.pre_launch.num_merges > sh.num_merges
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    ref, scores, L, _ = run_oracle(w)
+    checker.compare(a, ref, scores, L)
+
+
 def test_decode_replan_in_place():
     """Persistent plan/workspace re-planned with new lengths give the same
     result as a fresh allocation."""
