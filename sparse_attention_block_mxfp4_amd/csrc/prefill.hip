@@ -28,7 +28,7 @@
 
 namespace mi_idx {
 
-constexpr int kTileCols = 256;          // query columns per workgroup
+constexpr int kTileCols = 256;          // query columns per row tile
 constexpr int kPreHeaderInts = 16;
 constexpr int kChunks = kPageBytes / 16;                    // 544 16-byte chunks
 constexpr int kXcds = 8;                // MI355X accelerator complex dies
