@@ -129,12 +129,12 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // B operands: columns (wave*CGW + cg)*16 + t16.
     v8i bq[kBf16 ? 1 : CGW];
     u32x4 bqh[kBf16 ? CGW : 1][4];
-  #pragma unroll
+#pragma unroll
     for (int cg = 0; cg < CGW; ++cg) {
       const int col = (wave * CGW + cg) * 16 + t16;
       const int rl = col / H, h = col - rl * H;
       if constexpr (kBf16) {
-  #pragma unroll
+#pragma unroll
         for (int k = 0; k < 4; ++k) bqh[cg][k] = u32x4{0u, 0u, 0u, 0u};
       } else {
         bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -255,21 +255,21 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         // bf16 k-steps), then every column group runs its four-MFMA chain;
         // tile tl's chains go into one accumulator set while tile tl-1's are
         // folded, as in the E4M3 path.
-  #pragma unroll
+#pragma unroll
         for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
         v4f cx[CGW], cy[CGW];
-  #pragma unroll
+#pragma unroll
         for (int tl = 0; tl < 8; ++tl) {
           const uint8_t *tp = pg + page_token(tl, t16) * kTokenBytes;
           const uint32_t *a32 = reinterpret_cast<const uint32_t *>(tp + 16 * g);
           const float sf = e8m0_scale(tp[64 + g]);
           bf16x8 av[4];
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < 4; ++k) av[k] = fp4x8_to_bf16(a32[k], sf);
-  #pragma unroll
+#pragma unroll
           for (int cg = 0; cg < CGW; ++cg) {
             v4f c = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
             for (int k = 0; k < 4; ++k)
               c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k], __builtin_bit_cast(bf16x8, bqh[cg][k]),
                                                           c, 0, 0, 0);
@@ -282,27 +282,27 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
             }
           }
         }
-  #pragma unroll
+#pragma unroll
         for (int cg = 0; cg < CGW; ++cg) m[cg] = fold4(m[cg], cy[cg]);
         return;
       }
       u32x4 A[8];
       uint32_t S[8];
-  #pragma unroll
+#pragma unroll
       for (int tl = 0; tl < 8; ++tl) {
         const uint8_t *tp = pg + page_token(tl, t16) * kTokenBytes;
         const u32x4a4 a4 = *reinterpret_cast<const u32x4a4 *>(tp + 16 * g);
         A[tl] = u32x4{a4.x, a4.y, a4.z, a4.w};
         S[tl] = tp[64 + g];
       }
-  #pragma unroll
+#pragma unroll
       for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
       v4f cx[CGW], cy[CGW];
-  #pragma unroll
+#pragma unroll
       for (int cg = 0; cg < CGW; ++cg) cx[cg] = tile_mfma(A[0], cg, S[0]);
-  #pragma unroll
+#pragma unroll
       for (int tl = 1; tl < 8; ++tl) {
-  #pragma unroll
+#pragma unroll
         for (int cg = 0; cg < CGW; ++cg) {
           if (tl & 1) {
             cy[cg] = tile_mfma(A[tl], cg, S[tl]);
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
           }
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int cg = 0; cg < CGW; ++cg) m[cg] = fold4(m[cg], cy[cg]);
     };
     // The reduction over the 4 lane groups (token quarters) with VALU lane
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // folded maxima, so the compiler cannot sink the chain past the barrier
     // into the next step (where it would stay live across a queue drain).
     auto pin = [&](float (&m)[CGW]) {
-  #pragma unroll
+#pragma unroll
       for (int cg = 0; cg < CGW; ++cg) asm volatile("" : "+v"(m[cg]));
     };
     auto page_reduce = [&](const float (&m)[CGW]) -> float {
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // Insert every queued key into its column's list; each wave runs as many
     // insertions as its fullest queue holds.
     auto drain = [&]() {
-  #pragma unroll 1
+#pragma unroll 1
       for (int i = 0; i < kQueue; ++i) {
         if (!__any(i < nq)) break;
         const uint64_t v = s_queue[i][qslot];
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     const int K = (je - jb + NS - 1) / NS;
     if (K > 0) {
       float ma[CGW], mb[CGW];
-  #pragma unroll
+#pragma unroll
       for (int cg = 0; cg < CGW; ++cg) mb[cg] = -INFINITY;
       if constexpr (NS == 2) {
         s_floor[0][stream][tid] = 0ull;
@@ -487,12 +487,12 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       // pages, so inserting one list into the other gives the top-15 of both.
       uint64_t *s_lists = reinterpret_cast<uint64_t *>(&s_page[0][0][0]);
       if (stream == 1) {
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < kHist; ++i) s_lists[i * NT + tid] = top.k[i];
       }
       lds_barrier();
       if (stream == 0) {
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < kHist; ++i) top.insert_nb(s_lists[i * NT + tid]);
       }
     }
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       } else if (ws_lists != nullptr && fslot < kMaxSlots) {
         u32x4 *dst = reinterpret_cast<u32x4 *>(ws_lists + ((size_t)fslot * kTileCols + mycol) *
                                                             kListKeys);
-  #pragma unroll
+#pragma unroll
         for (int k2 = 0; k2 < kListKeys / 2; ++k2) {
           const uint64_t x0 = top.k[2 * k2];
           const uint64_t x1 = 2 * k2 + 1 < kHist ? top.k[2 * k2 + 1] : 0ull;
