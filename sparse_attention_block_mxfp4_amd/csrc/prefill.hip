@@ -21,6 +21,7 @@
 // device-wide fence is needed).
 #include <algorithm>
 #include <atomic>
+#include <queue>
 #include <cmath>
 #include <vector>
 
@@ -689,18 +690,24 @@ extern "C" int mi_idx_plan_prefill(const int32_t *cu_seqlens_q_host, const int32
   std::stable_sort(tiles.begin(), tiles.end(), [](const Tile &a, const Tile &b) {
     return a.r != b.r ? a.r < b.r : a.pages > b.pages;
   });
-  // Work lists: the tiles, in that order, are poured into at most S lists of
-  // capacity `cap` (planning cost = pages + kPieceCost per piece).  When the
-  // longest tile is within 5 % above the balanced share, tiles stay whole
-  // (cap = the longest tile; a tile that does not fit opens the next list).
-  // Otherwise cap starts at the share and a tile that does not fit is split
-  // when at least kMinSplit of its pages fit (or the list is still empty),
-  // else it opens the next list.  cap grows by 1/64 until S lists suffice;
-  // the whole-tile mode falls back to splitting when it needs more lists.
+  // Work lists, one per resident scorer workgroup (S), of equal planning cost
+  // (pages + kPieceCost per piece).  Near-equal tiles (the longest within 5 %
+  // above the balanced share), no more than S of them, stay whole, one per
+  // list.  Otherwise the tiles go longest first to the least-loaded list, and
+  // then, while it lowers the maximum, the largest piece of the most-loaded
+  // list gives a page range from its end to the least-loaded list (at most S
+  // such splits, each piece at least kMinSplit pages).  Lists are ordered by
+  // the request of their first piece, for the placement below; empty lists
+  // are dropped.
   const int S = resident_lists();
   struct Piece { int tile, pa, pe; };
-  std::vector<Piece> pieces;
+  std::vector<Piece> pieces;     // grouped by list, lists in launch order
   std::vector<int> list_first;
+  std::vector<int> slot;
+  struct Split { int tile, first_slot, nslots; };
+  std::vector<Split> splits;
+  int nslots = 0;
+  int nlists = 0;
   {
     int64_t work = 0, longest = 0;
     for (const Tile &t : tiles) {
@@ -708,66 +715,107 @@ extern "C" int mi_idx_plan_prefill(const int32_t *cu_seqlens_q_host, const int32
       longest = std::max(longest, (int64_t)t.pages + kPieceCost);
     }
     const int64_t share = std::max<int64_t>((work + S - 1) / S, kPieceCost + kMinSplit);
-    bool whole = longest > share && longest * 20 <= share * 21;
-    int64_t cap = whole ? longest : share;
-    for (;;) {
-      pieces.clear();
-      list_first.assign(1, 0);
-      int64_t used = 0;
+    const bool whole = (longest <= share || longest * 20 <= share * 21) && (int)tiles.size() <= S;
+    struct P { int tile, pa, pe, list; };
+    std::vector<P> ps;
+    ps.reserve(tiles.size() + S);
+    std::vector<int> head(S, -1);      // a list's first (largest) piece
+    if (whole) {
       for (int ti = 0; ti < (int)tiles.size(); ++ti) {
-        int a = 0;
-        const int P = tiles[ti].pages;
-        for (;;) {
-          const int64_t room = cap - used;
-          const bool empty = (int)pieces.size() == list_first.back();
-          if ((int64_t)(P - a) + kPieceCost <= room) {
-            pieces.push_back({ti, a, P});
-            used += (int64_t)(P - a) + kPieceCost;
-            break;
-          }
-          const int64_t fit = room - kPieceCost;
-          if (empty || (!whole && fit >= kMinSplit)) {
-            pieces.push_back({ti, a, a + (int)fit});   // fit < P - a
-            a += (int)fit;
-          }
-          list_first.push_back((int)pieces.size());   // the next list
-          used = 0;
-        }
+        head[ti] = (int)ps.size();
+        ps.push_back({ti, 0, tiles[ti].pages, ti});
       }
-      if ((int)pieces.size() == list_first.back()) list_first.pop_back();   // empty last list
-      if ((int)list_first.size() <= S) break;
-      if (whole) {
-        whole = false;
-        cap = share;
-      } else {
-        cap += std::max<int64_t>(1, cap / 64);
+    } else {
+      std::vector<int64_t> load(S, 0);
+      std::vector<int> order(tiles.size());
+      for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+      std::stable_sort(order.begin(), order.end(),
+                       [&](int x, int y) { return tiles[x].pages > tiles[y].pages; });
+      using LI = std::pair<int64_t, int>;
+      std::priority_queue<LI, std::vector<LI>, std::greater<LI>> lo;   // least-loaded first
+      for (int i = 0; i < S; ++i) lo.push({0, i});
+      for (int ti : order) {
+        const int i = lo.top().second;
+        lo.pop();
+        if (head[i] < 0) head[i] = (int)ps.size();
+        ps.push_back({ti, 0, tiles[ti].pages, i});
+        load[i] += (int64_t)tiles[ti].pages + kPieceCost;
+        lo.push({load[i], i});
+      }
+      // Rebalance with two heaps over (load, list); an entry whose load is
+      // no longer the list's is stale and skipped.
+      std::priority_queue<LI> hi;                                   // most-loaded first
+      for (int i = 0; i < S; ++i) hi.push({load[i], i});
+      auto top_of = [&](auto &h) {
+        while (h.top().first != load[h.top().second]) h.pop();
+        return h.top().second;
+      };
+      for (int it = 0; it < S; ++it) {
+        const int mx = top_of(hi), mn = top_of(lo);
+        if (mx == mn || head[mx] < 0) break;
+        P &pc = ps[head[mx]];
+        int64_t X = (load[mx] - load[mn] - kPieceCost) / 2;
+        X = std::min<int64_t>(X, (int64_t)(pc.pe - pc.pa) - kMinSplit);
+        if (X < kMinSplit) break;
+        const int cut = pc.pe - (int)X;
+        if (head[mn] < 0) head[mn] = (int)ps.size();
+        ps.push_back({pc.tile, cut, ps[head[mx]].pe, mn});
+        ps[head[mx]].pe = cut;
+        load[mx] -= X;
+        load[mn] += X + kPieceCost;
+        hi.push({load[mx], mx});
+        hi.push({load[mn], mn});
+        lo.push({load[mx], mx});
+        lo.push({load[mn], mn});
       }
     }
+    // Launch order of the non-empty lists: by the request of their first
+    // piece (stable), then each list's pieces in the order they were added.
+    std::vector<int> lorder;
+    for (int i = 0; i < S; ++i)
+      if (head[i] >= 0) lorder.push_back(i);
+    std::stable_sort(lorder.begin(), lorder.end(), [&](int x, int y) {
+      return tiles[ps[head[x]].tile].r < tiles[ps[head[y]].tile].r;
+    });
+    nlists = (int)lorder.size();
+    std::vector<int> pos(S, -1), count(nlists + 1, 0);
+    for (int k = 0; k < nlists; ++k) pos[lorder[k]] = k;
+    for (const P &q : ps) ++count[pos[q.list] + 1];
+    for (int k = 0; k < nlists; ++k) count[k + 1] += count[k];
+    list_first.assign(count.begin(), count.begin() + nlists);
+    pieces.resize(ps.size());
+    std::vector<int> at(ps.size());
+    for (int i = 0; i < (int)ps.size(); ++i) {
+      const int k = count[pos[ps[i].list]]++;
+      pieces[k] = {ps[i].tile, ps[i].pa, ps[i].pe};
+      at[i] = k;
+    }
+    // Slots: consecutive per split tile, in page order.
+    std::vector<int> by_tile(ps.size());
+    for (int i = 0; i < (int)ps.size(); ++i) by_tile[i] = i;
+    std::sort(by_tile.begin(), by_tile.end(), [&](int x, int y) {
+      return ps[x].tile != ps[y].tile ? ps[x].tile < ps[y].tile : ps[x].pa < ps[y].pa;
+    });
+    slot.assign(pieces.size(), -1);
+    for (size_t i = 0; i < by_tile.size();) {
+      size_t j = i + 1;
+      while (j < by_tile.size() && ps[by_tile[j]].tile == ps[by_tile[i]].tile) ++j;
+      if (j - i > 1) {
+        splits.push_back({ps[by_tile[i]].tile, nslots, (int)(j - i)});
+        for (size_t k = i; k < j; ++k) slot[at[by_tile[k]]] = nslots++;
+      }
+      i = j;
+    }
   }
-  const int nlists = (int)list_first.size();
   // Placement.  Workgroup b runs on XCD b % kXcds, each XCD with its own L2,
-  // and consecutive lists hold the tiles of one request (which read the same
-  // pages), so consecutive lists go to one XCD: XCD x takes the next
-  // count(x) lists as workgroups x, x + kXcds, ...
+  // and lists in request order put a request's tiles (which read the same
+  // pages) close together, so consecutive lists go to one XCD: XCD x takes
+  // the next count(x) lists as workgroups x, x + kXcds, ...
   std::vector<int> list_at(nlists);
   {
     int i = 0;
     for (int x = 0; x < kXcds; ++x)
       for (int b = x; b < nlists; b += kXcds) list_at[b] = i++;
-  }
-  // Slots for the pieces of split tiles (consecutive per tile).
-  std::vector<int> slot(pieces.size(), -1);
-  struct Split { int tile, first_slot, nslots; };
-  std::vector<Split> splits;
-  int nslots = 0;
-  for (size_t i = 0; i < pieces.size();) {
-    size_t j = i + 1;
-    while (j < pieces.size() && pieces[j].tile == pieces[i].tile) ++j;
-    if (j - i > 1) {
-      splits.push_back({pieces[i].tile, nslots, (int)(j - i)});
-      for (size_t k = i; k < j; ++k) slot[k] = nslots++;
-    }
-    i = j;
   }
   if (nlists > kMaxLists || nslots > kMaxSlots || splits.size() > (size_t)kMaxLists ||
       pieces.size() > tiles.size() + kMaxLists)

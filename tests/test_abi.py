@@ -232,10 +232,11 @@ def _plan_host(m, cu, sl, H, budget):
 
 def _check_plan(words, n_lists, n_chunks, n_merges, cu, sl, H, budget):
     """Every row in exactly one tile of M rows; each tile's pieces split its
-    pages [0, pages) into consecutive ranges; split tiles carry consecutive
-    slots and one merge record; work lists hold consecutive pieces; chunks
-    follow in order.  Returns the list costs (pages + 32 per piece)."""
-    R = len(sl)
+    pages [0, pages) into consecutive ranges, with slots consecutive in page
+    order and one merge record when split; work lists hold consecutive
+    pieces and come in request order of their first piece; the chunk count
+    is the pages' greedy rule.  Returns the list costs (pages + 32 per
+    piece)."""
     qn = np.diff(cu)
     M = 256 // H
     assert words[0] == n_lists and words[1] == M and words[2] == H and words[3] == n_chunks
@@ -254,15 +255,13 @@ def _check_plan(words, n_lists, n_chunks, n_merges, cu, sl, H, budget):
     splits = words[soff:soff + 8 * n_split].reshape(-1, 8)
     want_chunks = oracle.prefill_chunks(sl, budget if budget > 0 else 10 ** 12)
     assert n_chunks == len(want_chunks)
-    chunk_of = np.zeros(R, dtype=int)
-    for c, (a, b, _) in enumerate(want_chunks):
-        chunk_of[a:b] = c
     cover = [np.zeros(q, dtype=int) for q in qn]
     ranges = {}
     for r, row0, nr, pa, pe, slot, _, _ in pieces:
         assert 0 < nr <= M and row0 % M == 0
         ranges.setdefault((r, row0, nr), []).append((pa, pe, slot))
     for (r, row0, nr), rs in ranges.items():
+        rs.sort()
         cover[r][row0:row0 + nr] += 1
         pages = max((sl[r] - qn[r] + row0 + nr - 1) // 128, 0)
         assert rs[0][0] == 0 and rs[-1][1] == pages
@@ -278,10 +277,10 @@ def _check_plan(words, n_lists, n_chunks, n_merges, cu, sl, H, budget):
     assert all(np.all(c == 1) for c in cover)
     assert len(splits) == sum(1 for rs in ranges.values() if len(rs) > 1)
     assert n_slots == sum(len(rs) for rs in ranges.values() if len(rs) > 1)
-    # chunks are launched in order (the tile order inside a chunk is a
-    # placement choice and is not part of the contract)
-    ch_seq = [chunk_of[p[0]] for p in pieces]
-    assert ch_seq == sorted(ch_seq)
+    # lists in piece order start with requests in order (the placement puts
+    # a request's lists on neighbouring workgroups of one XCD)
+    firsts = [int(pieces[f][0]) for f, _, _, _ in sorted(lists.tolist())]
+    assert firsts == sorted(firsts)
     return [int(sum(p[4] - p[3] + 32 for p in pieces[f:f + c])) for f, c, _, _ in lists]
 
 

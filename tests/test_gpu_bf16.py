@@ -15,7 +15,8 @@ pytestmark = pytest.mark.gpu
 
 SMALL_BF16 = ["tiny_decode", "decode_batch_small", "multi_token_small", "ragged_prefill_small",
               "mixed_small", "edge_short", "edge_wide", "edge_prefill", "edge_heads5",
-              "prefill_h1_small", "prefill_h8_small", "prefill_many_tiles"]
+              "prefill_h1_small", "prefill_h8_small", "prefill_many_tiles",
+              "prefill_split_small"]
 
 
 @pytest.mark.parametrize("name", SMALL_BF16)

@@ -90,6 +90,12 @@ CONFIGS = {
     # several pieces, whole tiles and page ranges of split tiles mixed
     "prefill_many_tiles": dict(prefill=dict(R=6, new=3200, ctx_lo=0, ctx_hi=2000), H=4,
                                budget=0),
+    # one long tile among 300 short ones (more tiles than lists): the long
+    # tile is split into page ranges that join lists already holding short
+    # tiles (merges inside multi-piece lists)
+    "prefill_split_small": dict(prefill=dict(ctx=[0, 0, 0, 0, 0, 30000],
+                                             new=[3840, 3840, 3840, 3840, 3840, 64]), H=4,
+                                budget=0),
     # monotone-score cases (tests give them constructed K and Q; see
     # tests/test_gpu_trends.py): long histories in which every page is, or
     # no page after the first 15 is, a new top-15 entry
