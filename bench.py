@@ -328,9 +328,9 @@ def summarize_profiles(d, workload):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {a.gpus} is not supported by this build "
-              "(the multi-GPU sharding is described in DESIGN.md, not implemented).",
-              file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {a.gpus} is not supported: sharding over "
+              "several GPUs (decode by pages with one all-gather of the partial lists, "
+              "prefill by row tiles) is designed but not implemented.", file=sys.stderr)
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
