@@ -1,0 +1,44 @@
+/*
+ * mi_idx_probe.h -- HBM read-ceiling probes of one MI355X (libmi_idx_probe.so).
+ *
+ * Measurement aids, not part of the indexer: the pages define no such
+ * operation.  The benchmark times them next to the decode phase, so that its
+ * bandwidth is reported against both the 8 TB/s specification figure and
+ * what a plain read of HBM reaches on the same GPU.  Conventions as in
+ * mi_idx.h: device pointers, asynchronous on `stream` (a hipStream_t as
+ * void*), nothing allocated, no synchronization.  Each returns 0 on success,
+ * 1 for a bad argument, 3 when `sink` is too small, 4 for a HIP error.
+ */
+#ifndef MI_IDX_PROBE_H
+#define MI_IDX_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads the `bytes` bytes at `buf` (16-byte aligned; bytes rounded down to a
+ * multiple of 16) once, as coalesced 16-byte loads, with 8 workgroups of 256
+ * threads per compute unit.  sink: >= 2048 * CUs uint32 words of scratch the
+ * kernel practically never writes. */
+int mi_idx_probe_read_stream(const void *buf, int64_t bytes, uint32_t *sink,
+                             int64_t sink_words, void *stream);
+
+/* Reads n_order whole 8704-byte pages of `pages` ([num_pages, 8704], 16-byte
+ * aligned) in the order of `order` (int32 page ids; an id outside
+ * [0, num_pages) is clamped into it): wave w reads entries
+ * [w * per_wave, (w + 1) * per_wave) one page after another, all 544 chunks
+ * of a page in flight at once and the next page issued before the current
+ * one is consumed.  sink: >= 256 * ceil(waves / 4) words, waves =
+ * ceil(n_order / per_wave). */
+int mi_idx_probe_read_pages(const uint8_t *pages, int64_t num_pages,
+                            const int32_t *order, int64_t n_order, int per_wave,
+                            uint32_t *sink, int64_t sink_words, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI_IDX_PROBE_H */

@@ -34,6 +34,7 @@ _SIGS = {
                                                 _i32, _i32]),
     "mi_idx_insert_mxfp4": (_i32, [_vp, _i32, _i64, _vp, _i64, _vp, _i64, _vp]),
     "mi_idx_decode_plan_bytes": (_sz, [_i32]),
+    "mi_idx_decode_plan_capacity": (_sz, [_i32, _i32, _i32, _i32]),
     "mi_idx_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "mi_idx_plan_decode": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _sz, _vp]),
     "mi_idx_score_topk_decode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
@@ -174,6 +175,11 @@ def mi_idx_decode_plan_bytes(max_reqs):
     return int(lib.mi_idx_decode_plan_bytes(max_reqs))
 
 
+def mi_idx_decode_plan_capacity(max_reqs, max_pages, query_len, num_heads):
+    """Work items (rows of four int32) of a decode plan for max_reqs requests."""
+    return int(lib.mi_idx_decode_plan_capacity(max_reqs, max_pages, query_len, num_heads))
+
+
 def mi_idx_decode_workspace_bytes(max_reqs, query_len, num_heads):
     return int(lib.mi_idx_decode_workspace_bytes(max_reqs, query_len, num_heads))
 
@@ -194,6 +200,19 @@ def mi_idx_score_topk_decode(q, pages, block_table, seq_lens, query_len, max_pag
     """q [R*query_len, H, 128] E4M3 (uint8 or float8_e4m3fn) or bfloat16;
     topk_out [R*query_len, H, 16] int32; block_table [R, >=max_pages] int32
     (row stride taken from the tensor)."""
+    R, H = _decode_args(q, pages, block_table, seq_lens, query_len, max_pages, topk_out,
+                        scores_out)
+    _need(plan, "plan", _U8)
+    _need(workspace, "workspace", _U8)
+    st = lib.mi_idx_score_topk_decode(
+        _ptr(q), _q_dtype(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
+        block_table.stride(0), _ptr(seq_lens), R, query_len, H, max_pages, float(scale),
+        _ptr(plan), plan.numel(), _ptr(workspace), workspace.numel(), _ptr(topk_out),
+        _ptr(scores_out), _stream(stream))
+    _check(st, "mi_idx_score_topk_decode")
+
+
+def _decode_args(q, pages, block_table, seq_lens, query_len, max_pages, topk_out, scores_out):
     _need(q, "q", _QALL)
     _need(pages, "pages", _U8)
     _need(block_table, "block_table", _I32, contiguous=False)
@@ -213,12 +232,7 @@ def mi_idx_score_topk_decode(q, pages, block_table, seq_lens, query_len, max_pag
         _need(scores_out, "scores_out", (torch.float32,))
         if tuple(scores_out.shape) != (R * query_len, H, max_pages):
             raise ValueError("scores_out must be [rows, H, max_pages]")
-    st = lib.mi_idx_score_topk_decode(
-        _ptr(q), _q_dtype(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
-        block_table.stride(0), _ptr(seq_lens), R, query_len, H, max_pages, float(scale),
-        _ptr(plan), plan.numel(), _ptr(workspace), workspace.numel(), _ptr(topk_out),
-        _ptr(scores_out), _stream(stream))
-    _check(st, "mi_idx_score_topk_decode")
+    return R, H
 
 
 def mi_idx_prefill_plan_bytes(num_reqs, total_q, num_heads):

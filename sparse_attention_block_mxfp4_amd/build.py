@@ -13,6 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["api.hip", "insert.hip", "decode.hip", "prefill.hip", "select.hip"]
 LIB = os.path.join(HERE, "libmi_idx.so")
+# HBM read-ceiling probes (a measurement aid of the benchmark, not the indexer)
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libmi_idx_probe.so")
 
 
 def hipcc():
@@ -31,9 +34,10 @@ PER_SOURCE = {"prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 def _flags():
     return ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # device code: no NaN operands reach max/compare (keys test NaN on
-            # the bits), MFMA results stay in VGPRs
-            "-Xarch_device", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
+            # MFMA results stay in VGPRs.  NaN is honoured: page maxima
+            # propagate it (IEEE maximum), which -fno-honor-nans would let the
+            # compiler turn back into the NaN-dropping max.
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", os.path.join(ROOT, "include")]
 
 
@@ -46,15 +50,13 @@ def _run(cmd, verbose):
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
 
 
-def build(verbose=False, extra=()):
-    """Compile every source (one object each, with its own flags) and link
-    them into libmi_idx.so; the library is replaced only when all succeed."""
+def _build_lib(sources, lib, verbose, extra):
     from concurrent.futures import ThreadPoolExecutor
-    tmp = LIB + ".tmp"
-    objs = [os.path.join(HERE, "_build_" + name.replace(".hip", ".o")) for name in SOURCES]
+    tmp = lib + ".tmp"
+    objs = [os.path.join(HERE, "_build_" + name.replace(".hip", ".o")) for name in sources]
     try:
         cmds = [[hipcc(), *_flags(), *PER_SOURCE.get(name, []), *extra, "-c",
-                 os.path.join(HERE, "csrc", name), "-o", obj] for name, obj in zip(SOURCES, objs)]
+                 os.path.join(HERE, "csrc", name), "-o", obj] for name, obj in zip(sources, objs)]
         with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
             for f in [ex.submit(_run, c, verbose) for c in cmds]:
                 f.result()
@@ -63,7 +65,16 @@ def build(verbose=False, extra=()):
         for obj in objs:
             if os.path.exists(obj):
                 os.remove(obj)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose=False, extra=()):
+    """Compile every source (one object each, with its own flags) and link
+    them into libmi_idx.so, and the probes into libmi_idx_probe.so; a library
+    is replaced only when all its sources compile."""
+    _build_lib(SOURCES, LIB, verbose, extra)
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose, extra)
     return LIB
 
 

@@ -93,13 +93,22 @@ __device__ __forceinline__ void load_q_bf16(const uint8_t *qrow, int g, u32x4 (&
     b[s] = *reinterpret_cast<const u32x4 *>(qrow + 2 * (32 * g + 8 * s));
 }
 
+// Page maxima propagate NaN: a token whose q.k is NaN (an E8M0 scale byte
+// 0xFF, a NaN query element) makes its page's score NaN, which the selection
+// keys rank below every number.  IEEE 754-2019 maximum (gfx950:
+// v_maximum3_f32, three operands like v_max3_f32), never the NaN-dropping
+// fmax.
+__device__ __forceinline__ float nmax(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 __device__ __forceinline__ float max4(const v4f &c) {
-  return fmaxf(fmaxf(c.x, c.y), fmaxf(c.z, c.w));
+  return nmax(nmax(c.x, c.y), nmax(c.z, c.w));
 }
 
 // m = max(m, c.x, c.y, c.z, c.w) as two 3-input maxima.
 __device__ __forceinline__ float fold4(float m, const v4f &c) {
-  return fmaxf(fmaxf(fmaxf(fmaxf(m, c.x), c.y), c.z), c.w);
+  return nmax(nmax(nmax(nmax(m, c.x), c.y), c.z), c.w);
 }
 
 // Selection key: larger is better.  High word = the score's bits mapped to
@@ -153,25 +162,25 @@ struct TopList {
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return nmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return nmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 // Lanes 0..31 get max(a, a of lane+32), lanes 32..63 get max(b, b of lane-32).
 __device__ __forceinline__ float max_split32(float a, float b) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return nmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 // Even 16-lane rows get max(a, a of the next row), odd rows get max(b, b of
 // the previous row).
 __device__ __forceinline__ float max_split16(float a, float b) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return nmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Workgroup barrier that orders LDS accesses only: global loads in flight
@@ -180,6 +189,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Local page of a row at position p, or -1 for a row that gets no selection:
+// a padding row (p < 0) or a row whose causal history runs past the
+// max_pages block-table columns the caller vouches for (refused: its history
+// cannot be read).
+__device__ __forceinline__ int local_page(int p, int max_pages) {
+  return (p >= 0 && (p >> 7) <= max_pages) ? (p >> 7) : -1;
 }
 
 // Write one (row, head) output: ranked ids, -1 padding, then the local page.

@@ -89,10 +89,15 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
   const int per = (num_reqs + kPlanThreads - 1) / kPlanThreads;
   const int r0 = min(num_reqs, tid * per), r1 = min(num_reqs, r0 + per);
   long long hsum = 0;
-  for (int r = r0; r < r1; ++r) hsum += history_of(seq_lens, r, max_pages);
+  int over = 0;   // a request whose history goes past max_pages block-table columns
+  for (int r = r0; r < r1; ++r) {
+    hsum += history_of(seq_lens, r, max_pages);
+    const int sl = seq_lens[r];
+    over |= sl >= 1 && ((sl - 1) >> 7) > max_pages;
+  }
   hsum = wave_sum(hsum);
   if (lane == 0) s_wave[0][wave] = hsum;
-  __syncthreads();
+  over = __syncthreads_or(over);
   long long total = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) total += s_wave[0][w];
@@ -165,7 +170,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(
     plan[3] = query_len;
     plan[4] = max_pages;
     plan[5] = capacity;
-    reinterpret_cast<uint32_t *>(ws)[0] = total_items > capacity ? 2u : 0u;   // error bits
+    // error bits: 1 = plan overflow, 2 = rows refused for a history past max_pages
+    reinterpret_cast<uint32_t *>(ws)[0] = (total_items > capacity ? 2u : 0u) | (over ? 4u : 0u);
   }
 }
 
@@ -220,7 +226,7 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
       const int p = sl - query_len + i;
-      Lc[cg] = p >= 0 ? min(p >> 7, max_pages) : -1;
+      Lc[cg] = local_page(p, max_pages);
     }
   }
   TopList top[NCG];
@@ -280,14 +286,14 @@ __global__ __launch_bounds__(256) void decode_score_kernel(
           for (int tile = 0; tile < 8; ++tile) {
 #pragma unroll
             for (int cg = 0; cg < NCG; ++cg)
-              m[cg] = fmaxf(m[cg], max4(kBf16 ? mfma_fp4_bf16(a[u][tile], bqh[kBf16 ? cg : 0], s[u][tile])
+              m[cg] = nmax(m[cg], max4(kBf16 ? mfma_fp4_bf16(a[u][tile], bqh[kBf16 ? cg : 0], s[u][tile])
                                               : mfma_fp4_fp8(a[u][tile], bq[cg], s[u][tile])));
           }
 #pragma unroll
           for (int cg = 0; cg < NCG; ++cg) {
             float v = m[cg];
-            v = fmaxf(v, __shfl_xor(v, 16, 64));
-            v = fmaxf(v, __shfl_xor(v, 32, 64));
+            v = nmax(v, __shfl_xor(v, 16, 64));
+            v = nmax(v, __shfl_xor(v, 32, 64));
             if (j < Lc[cg]) {
               top[cg].insert(make_key(v, j));
               if (kScores && g == 0) {
@@ -387,9 +393,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
   const int qi = c / H, h = c - qi * H;
   const int64_t T = (int64_t)r * query_len + qi;
   const int p = seq_lens[r] - query_len + qi;
-  const int L = p >= 0 ? min(p >> 7, max_pages) : -1;
+  const int L = local_page(p, max_pages);
   int32_t *dst = out + (T * H + h) * kTopk;
-  if (L < 0) {   // a padding row: every slot empty
+  if (L < 0) {   // a padding or refused row: every slot empty
     if (lane < kTopk) dst[lane] = -1;
     return;
   }
@@ -486,6 +492,14 @@ extern "C" size_t mi_idx_decode_plan_bytes(int max_reqs) {
   return (size_t)kPlanHeaderInts * 4 + decode_capacity(max_reqs) * kItemInts * 4;
 }
 
+extern "C" size_t mi_idx_decode_plan_capacity(int max_reqs, int max_pages, int query_len,
+                                              int num_heads) {
+  if (max_reqs < 0 || max_pages < 0 || query_len < 1 || query_len > MI_IDX_MAX_QUERY_LEN ||
+      num_heads < 1 || num_heads > MI_IDX_MAX_HEADS)
+    return 0;
+  return decode_capacity(max_reqs);
+}
+
 extern "C" size_t mi_idx_decode_workspace_bytes(int max_reqs, int query_len, int num_heads) {
   if (max_reqs < 0 || query_len < 1 || num_heads < 1) return 0;
   return lists_offset(max_reqs) + lists_bytes(decode_capacity(max_reqs), query_len * num_heads);
@@ -561,6 +575,77 @@ static int check_decode_sizes(const char *who, int num_reqs, int query_len, int 
   return MI_IDX_OK;
 }
 
+// The decode plan kernel on `plan` (capacity items) and `ws`; arguments
+// already checked.
+static int launch_plan(const int32_t *seq_lens, int num_reqs, int query_len, int num_heads,
+                       int max_pages, int32_t *plan, int cap, uint8_t *ws, hipStream_t s) {
+  const int resident = resident_items(query_len * num_heads);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, seq_lens, num_reqs,
+                     max_pages, query_len, cap, query_len * num_heads, resident, plan, ws);
+  return mi_idx_check_launch("plan_decode");
+}
+
+// The scorer and the merge on a plan of `cap` items; arguments already
+// checked.
+static int launch_score(const uint8_t *qb, int q_dtype, const uint8_t *pages,
+                        int64_t num_blocks, const int32_t *block_table, int64_t bt_stride,
+                        const int32_t *seq_lens, int num_reqs, int query_len, int num_heads,
+                        int max_pages, float scale, const int32_t *plan, int cap, uint8_t *ws,
+                        int32_t *topk_out, float *scores_out, hipStream_t s) {
+  const int rows = query_len * num_heads;
+  const int ncg = (rows + 15) / 16;
+  const dim3 grid((cap + 3) / 4), block(256);
+#define MI_IDX_LAUNCH_DEC1(N, SC, BF)                                                          \
+  hipLaunchKernelGGL((decode_score_kernel<N, SC, BF>), grid, block, 0, s, qb, pages,          \
+                     num_blocks, block_table, bt_stride, seq_lens, num_reqs, query_len,        \
+                     num_heads, max_pages, scale, plan, ws, scores_out)
+#define MI_IDX_LAUNCH_DEC(N)                                                                   \
+  if (q_dtype == MI_IDX_Q_BF16) {                                                              \
+    if (scores_out) MI_IDX_LAUNCH_DEC1(N, true, true);                                         \
+    else MI_IDX_LAUNCH_DEC1(N, false, true);                                                   \
+  } else {                                                                                     \
+    if (scores_out) MI_IDX_LAUNCH_DEC1(N, true, false);                                        \
+    else MI_IDX_LAUNCH_DEC1(N, false, false);                                                  \
+  }
+  switch (ncg) {
+    case 1: MI_IDX_LAUNCH_DEC(1); break;
+    case 2: MI_IDX_LAUNCH_DEC(2); break;
+    case 3: MI_IDX_LAUNCH_DEC(3); break;
+    default: MI_IDX_LAUNCH_DEC(4); break;
+  }
+#undef MI_IDX_LAUNCH_DEC
+#undef MI_IDX_LAUNCH_DEC1
+  int st = mi_idx_check_launch("score_topk_decode");
+  if (st) return st;
+  hipLaunchKernelGGL(decode_merge_kernel,
+                     dim3(num_reqs, (rows + kMergeWaves - 1) / kMergeWaves),
+                     dim3(64 * kMergeWaves), 0, s, seq_lens, num_reqs, query_len, num_heads,
+                     max_pages, ws, topk_out);
+  return mi_idx_check_launch("score_topk_decode (merge)");
+}
+
+// Checks of a score call's own arguments (the plan and workspace sizes are
+// checked by the caller).
+static int check_score_args(const char *who, const void *q, int q_dtype, const uint8_t *pages,
+                            int64_t num_blocks, const int32_t *block_table, int64_t bt_stride,
+                            const int32_t *seq_lens, int max_pages, float scale,
+                            const int32_t *topk_out) {
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return mi_idx_fail(MI_IDX_EINVAL, "%s: scale must be positive and finite", who);
+  if (q_dtype != MI_IDX_Q_E4M3 && q_dtype != MI_IDX_Q_BF16)
+    return mi_idx_fail(MI_IDX_EINVAL, "%s: q_dtype %d is neither E4M3 (0) nor bf16 (1)", who,
+                       q_dtype);
+  if (!q || !pages || !block_table || !seq_lens || !topk_out)
+    return mi_idx_fail(MI_IDX_EINVAL, "%s: null pointer", who);
+  if (((uintptr_t)q % 16) || ((uintptr_t)pages % 16) || ((uintptr_t)topk_out % 16))
+    return mi_idx_fail(MI_IDX_EINVAL, "%s: q, pages and topk_out must be 16-byte aligned", who);
+  if (num_blocks <= 0) return mi_idx_fail(MI_IDX_EINVAL, "%s: num_blocks <= 0", who);
+  if (bt_stride < max_pages)
+    return mi_idx_fail(MI_IDX_EINVAL, "%s: bt_stride %lld < max_pages %d", who,
+                       (long long)bt_stride, max_pages);
+  return MI_IDX_OK;
+}
+
 extern "C" int mi_idx_plan_decode(const int32_t *seq_lens, int num_reqs, int query_len,
                                   int num_heads, int max_pages, void *plan, size_t plan_bytes,
                                   void *workspace, size_t ws_bytes, void *stream) {
@@ -572,12 +657,8 @@ extern "C" int mi_idx_plan_decode(const int32_t *seq_lens, int num_reqs, int que
     return mi_idx_fail(MI_IDX_EINVAL, "plan_decode: null pointer");
   if (((uintptr_t)plan % 16) || ((uintptr_t)workspace % 16))
     return mi_idx_fail(MI_IDX_EINVAL, "plan_decode: plan and workspace must be 16-byte aligned");
-  const int cap = plan_capacity(plan_bytes);
-  const int resident = resident_items(query_len * num_heads);
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, (hipStream_t)stream, seq_lens,
-                     num_reqs, max_pages, query_len, cap, query_len * num_heads, resident,
-                     (int32_t *)plan, (uint8_t *)workspace);
-  return mi_idx_check_launch("plan_decode");
+  return launch_plan(seq_lens, num_reqs, query_len, num_heads, max_pages, (int32_t *)plan,
+                     plan_capacity(plan_bytes), (uint8_t *)workspace, (hipStream_t)stream);
 }
 
 extern "C" int mi_idx_score_topk_decode(const void *q, int q_dtype, const uint8_t *pages,
@@ -597,48 +678,16 @@ extern "C" int mi_idx_score_topk_decode(const void *q, int q_dtype, const uint8_
     return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: q_dtype %d is neither E4M3 (0) nor "
                                       "bf16 (1)", q_dtype);
   if (num_reqs == 0) return MI_IDX_OK;
-  if (!q || !pages || !block_table || !seq_lens || !plan || !workspace || !topk_out)
-    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: null pointer");
-  if (((uintptr_t)q % 16) || ((uintptr_t)pages % 16) || ((uintptr_t)topk_out % 16) ||
-      ((uintptr_t)workspace % 16) || ((uintptr_t)plan % 16))
-    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: q, pages, topk_out, plan and "
-                                      "workspace must be 16-byte aligned");
-  if (num_blocks <= 0) return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: num_blocks <= 0");
-  if (bt_stride < max_pages)
-    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: bt_stride %lld < max_pages %d",
-                       (long long)bt_stride, max_pages);
-  const int cap = plan_capacity(plan_bytes);
-  const int rows = query_len * num_heads;
-  const int ncg = (rows + 15) / 16;
-  const dim3 grid((cap + 3) / 4), block(256);
-  hipStream_t s = (hipStream_t)stream;
-  const uint8_t *qb = static_cast<const uint8_t *>(q);
-#define MI_IDX_LAUNCH_DEC1(N, SC, BF)                                                          \
-  hipLaunchKernelGGL((decode_score_kernel<N, SC, BF>), grid, block, 0, s, qb, pages,          \
-                     num_blocks, block_table, bt_stride, seq_lens, num_reqs, query_len,        \
-                     num_heads, max_pages, scale, (const int32_t *)plan, (uint8_t *)workspace, \
-                     scores_out)
-#define MI_IDX_LAUNCH_DEC(N)                                                                   \
-  if (q_dtype == MI_IDX_Q_BF16) {                                                              \
-    if (scores_out) MI_IDX_LAUNCH_DEC1(N, true, true);                                         \
-    else MI_IDX_LAUNCH_DEC1(N, false, true);                                                   \
-  } else {                                                                                     \
-    if (scores_out) MI_IDX_LAUNCH_DEC1(N, true, false);                                        \
-    else MI_IDX_LAUNCH_DEC1(N, false, false);                                                  \
-  }
-  switch (ncg) {
-    case 1: MI_IDX_LAUNCH_DEC(1); break;
-    case 2: MI_IDX_LAUNCH_DEC(2); break;
-    case 3: MI_IDX_LAUNCH_DEC(3); break;
-    default: MI_IDX_LAUNCH_DEC(4); break;
-  }
-#undef MI_IDX_LAUNCH_DEC
-#undef MI_IDX_LAUNCH_DEC1
-  st = mi_idx_check_launch("score_topk_decode");
+  st = check_score_args("score_topk_decode", q, q_dtype, pages, num_blocks, block_table,
+                        bt_stride, seq_lens, max_pages, scale, topk_out);
   if (st) return st;
-  hipLaunchKernelGGL(decode_merge_kernel,
-                     dim3(num_reqs, (query_len * num_heads + kMergeWaves - 1) / kMergeWaves),
-                     dim3(64 * kMergeWaves), 0, s, seq_lens, num_reqs,
-                     query_len, num_heads, max_pages, (const uint8_t *)workspace, topk_out);
-  return mi_idx_check_launch("score_topk_decode (merge)");
+  if (!plan || !workspace)
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: null pointer");
+  if (((uintptr_t)workspace % 16) || ((uintptr_t)plan % 16))
+    return mi_idx_fail(MI_IDX_EINVAL, "score_topk_decode: plan and workspace must be 16-byte "
+                                      "aligned");
+  return launch_score(static_cast<const uint8_t *>(q), q_dtype, pages, num_blocks, block_table,
+                      bt_stride, seq_lens, num_reqs, query_len, num_heads, max_pages, scale,
+                      (const int32_t *)plan, plan_capacity(plan_bytes), (uint8_t *)workspace,
+                      topk_out, scores_out, (hipStream_t)stream);
 }

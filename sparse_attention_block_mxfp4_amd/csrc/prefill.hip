@@ -31,6 +31,7 @@ namespace mi_idx {
 
 constexpr int kTileCols = 256;          // query columns per row tile
 constexpr int kPreHeaderInts = 16;
+constexpr int kPreErrWord = 9;          // plan header word of the error bits
 constexpr int kChunks = kPageBytes / 16;                    // 544 16-byte chunks
 constexpr int kXcds = 8;                // MI355X accelerator complex dies
 constexpr int kPrefillCgw = 4;          // 16-column groups per wave
@@ -47,7 +48,10 @@ inline int rows_per_tile(int H) { return kTileCols / H; }
 
 // Plan (int32 words).  Header: [0] work lists, [1] rows per tile,
 // [2] num_heads, [3] chunk count, [4] pieces, [5] word offset of the pieces,
-// [6] split tiles, [7] word offset of the split tiles, [8] partial-list slots.
+// [6] split tiles, [7] word offset of the split tiles, [8] partial-list slots,
+// [9] error bits of the score calls on this plan (written 0 by the plan's
+// copy; bit 0: a block-table id outside the pool was skipped, bit 2: a row
+// whose history runs past max_pages was refused).
 // Work list i (int4 at word 16 + 4 i): first piece, piece count.  Piece (8
 // words): request, first row (in the request), row count, first page, end
 // page (an upper bound; the kernel clamps it to the device lengths), slot
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ context_lens, int num_reqs, int64_t total_q, int H,
     int max_pages, float scale, const int32_t *__restrict__ plan, uint64_t *__restrict__ ws_lists,
-    int32_t *__restrict__ out, float *__restrict__ scores_out) {
+    int32_t *__restrict__ out, float *__restrict__ scores_out, uint32_t *err) {
   constexpr int NW = 16 / CGW;                       // waves per stream
   constexpr int NT = 64 * NW;                        // threads per stream
   constexpr int kLoads = (kChunks + NT - 1) / NT;    // 16-byte chunks per thread
@@ -169,9 +173,11 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     const int my_rl = mycol / H, my_h = mycol - my_rl * H;
     const int64_t myT = q0 + row0 + my_rl;
     int myL = -1;
+    bool refused = false;   // a row whose history runs past max_pages
     if (my_rl < nrows && myT < total_q) {
       const int p = ctx + row0 + my_rl;
-      myL = (p >= 0 && p < sl) ? min(p >> 7, max_pages) : -1;
+      myL = p < sl ? local_page(p, max_pages) : -1;
+      refused = p >= 0 && p < sl && myL < 0;
     }
     // Pages of the tile: every row's history is a prefix of 0..J-1.  This
     // piece walks pages jb..je-1 of them; a column takes page j < myLe.
@@ -229,8 +235,12 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // the block in between have already drained, whereas a scalar load here
     // would be waited for together with every outstanding LDS access.
     auto bt_fetch = [&](int step) -> int { return bt_entry(step + (lane & 1)); };
+    // an issued page id outside the pool (every issued page lies inside the
+    // piece's range): skipped, reported in the plan's error word
+    bool bad = false;
     auto pf_issue = [&](int step, int phys, uint4 &R0, uint4 &R1, uint4 &R2) {
       const bool valid = phys >= 0 && (int64_t)phys < num_blocks;
+      bad |= !valid;
       const uint64_t bit = 1ull << (step & 63);
       vmask = valid ? (vmask | bit) : (vmask & ~bit);
       // wave-uniform page base + this thread's 32-bit chunk offsets
@@ -482,6 +492,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       take(page_reduce(mb), k - 1, 0);
     }
     drain();
+    if (bad && lane == 0) atomicOr(err, 1u);
     if constexpr (NS == 2) {
       // Stream 1 hands its lists to stream 0 through the (now idle) page
       // buffers: key i of thread t at [i * NT + t].  The streams saw disjoint
@@ -498,8 +509,10 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       }
     }
     if (kOne) {
-      if (stream == 0 && writer && my_rl < nrows && myT < total_q)
+      if (stream == 0 && writer && my_rl < nrows && myT < total_q) {
         write_row(out + (myT * H + my_h) * kTopk, top, myL);
+        if (refused) atomicOr(err, 4u);
+      }
     } else if (stream == 0 && writer) {
       // The piece record and the column's row are read again here rather than
       // kept in registers across the page walk (the asm hides the earlier read).
@@ -512,8 +525,9 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       if (rl < f0.z && T < total_q) {
       if (fslot < 0) {
         const int p = context_lens[fr] + frow0 + rl;
-        const int L = (p >= 0 && p < seq_lens[fr]) ? min(p >> 7, max_pages) : -1;
+        const int L = p < seq_lens[fr] ? local_page(p, max_pages) : -1;
         write_row(out + (T * H + h) * kTopk, top, L);
+        if (L < 0 && p >= 0 && p < seq_lens[fr]) atomicOr(err, 4u);   // refused row
       } else if (ws_lists != nullptr && fslot < kMaxSlots) {
         u32x4 *dst = reinterpret_cast<u32x4 *>(ws_lists + ((size_t)fslot * kTileCols + mycol) *
                                                             kListKeys);
@@ -539,7 +553,7 @@ __global__ __launch_bounds__(kTileCols) void prefill_merge_kernel(
     const int32_t *__restrict__ cu_seqlens_q, const int32_t *__restrict__ seq_lens,
     const int32_t *__restrict__ context_lens, int num_reqs, int64_t total_q, int H,
     int max_pages, const int32_t *__restrict__ plan, const uint64_t *__restrict__ ws_lists,
-    int32_t *__restrict__ out) {
+    int32_t *__restrict__ out, uint32_t *err) {
   if ((int)blockIdx.x >= plan[6]) return;
   const int4 *splits = reinterpret_cast<const int4 *>(plan + plan[7]);
   const int4 m0 = splits[2 * blockIdx.x], m1 = splits[2 * blockIdx.x + 1];
@@ -551,7 +565,8 @@ __global__ __launch_bounds__(kTileCols) void prefill_merge_kernel(
   const int64_t T = (int64_t)cu_seqlens_q[r] + row0 + rl;
   if (T >= total_q) return;
   const int p = context_lens[r] + row0 + rl;
-  const int L = (p >= 0 && p < seq_lens[r]) ? min(p >> 7, max_pages) : -1;
+  const int L = p < seq_lens[r] ? local_page(p, max_pages) : -1;
+  if (L < 0 && p >= 0 && p < seq_lens[r]) atomicOr(err, 4u);   // refused row
   TopList top;
   top.clear();
 #pragma unroll 1
@@ -878,7 +893,7 @@ extern "C" int mi_idx_score_topk_prefill(const void *q, int q_dtype, const uint8
                                          int64_t bt_stride, const int32_t *cu_seqlens_q,
                                          const int32_t *seq_lens, const int32_t *context_lens,
                                          int num_reqs, int64_t total_q, int num_heads,
-                                         int max_pages, float scale, const void *plan,
+                                         int max_pages, float scale, void *plan,
                                          size_t plan_bytes, const mi_idx_prefill_launch *launch,
                                          void *workspace, size_t ws_bytes, int32_t *topk_out,
                                          float *scores_out, void *stream) {
@@ -922,13 +937,15 @@ extern "C" int mi_idx_score_topk_prefill(const void *q, int q_dtype, const uint8
                          mi_idx_prefill_workspace_bytes());
   }
   const dim3 grid(num_tiles), block(64 * kPrefillStreams * (16 / kPrefillCgw));
+  uint32_t *err = static_cast<uint32_t *>(plan) + kPreErrWord;
   const uint8_t *qb = static_cast<const uint8_t *>(q);
   uint64_t *lists = static_cast<uint64_t *>(workspace);
 #define MI_IDX_LAUNCH_PRE(SC, BF)                                                              \
   hipLaunchKernelGGL((prefill_score_kernel<kPrefillCgw, kPrefillStreams, SC, BF, MI_IDX_ONE>), grid, block, \
                      0, (hipStream_t)stream, qb, pages, num_blocks, block_table, bt_stride,    \
                      cu_seqlens_q, seq_lens, context_lens, num_reqs, total_q, num_heads,       \
-                     max_pages, scale, (const int32_t *)plan, lists, topk_out, scores_out)
+                     max_pages, scale, (const int32_t *)plan, lists, topk_out, scores_out,      \
+                     err)
   // one whole tile per work list: the single-pass instantiation
   const bool one = num_pieces == num_tiles && num_merges == 0;
   if (one) {
@@ -957,6 +974,6 @@ extern "C" int mi_idx_score_topk_prefill(const void *q, int q_dtype, const uint8
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(num_merges), dim3(kTileCols), 0,
                        (hipStream_t)stream, cu_seqlens_q, seq_lens, context_lens, num_reqs,
                        total_q, num_heads, max_pages, (const int32_t *)plan,
-                       (const uint64_t *)lists, topk_out);
+                       (const uint64_t *)lists, topk_out, err);
   return mi_idx_check_launch("score_topk_prefill");
 }

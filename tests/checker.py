@@ -9,13 +9,35 @@ Per (row, head), with L the row's local page (-1 for a padding row):
   pages (so only pages whose scores are within that tolerance may swap,
   in order or across the 15th place); ties of exactly equal score must keep
   the lower id, which this allows as a zero-difference swap only if the
-  GPU's pick is also a valid tie.
+  GPU's pick is also a valid tie;
+* NaN scores (pages with a NaN token) take no tolerance: the tolerance base is
+  the largest finite |score|, and at every rank the GPU's pick must be NaN
+  exactly when the oracle's is, and then the same page (NaN pages rank last,
+  by id).
 Returns the fraction of (row, head) outputs that match bit-exactly.
 """
 
 import numpy as np
 
 REL_TOL = 1e-4
+
+
+def _tol(s, rel_tol):
+    f = np.abs(s[np.isfinite(s)])
+    return rel_tol * (f.max() if f.size else 0.0)
+
+
+def _rank_gaps(ids_g, ids_o, s, tol):
+    """Per rank: whether the GPU's pick is acceptable against the oracle's."""
+    sg, so = s[ids_g], s[ids_o]
+    ng, no = np.isnan(sg), np.isnan(so)
+    ok = np.where(ng | no, ng & no & (ids_g == ids_o), True)
+    finite = ~(ng | no)
+    with np.errstate(invalid="ignore"):
+        diff = np.where(finite, np.abs(sg - so), 0.0)
+    # +inf / -inf picks must be the same value (their difference is NaN)
+    ok &= np.where(finite, (diff <= tol) | (sg == so), True)
+    return ok, sg - so
 
 
 def compare(gpu, ora, scores, L, rows=None, rel_tol=REL_TOL, gpu_scores=None):
@@ -43,18 +65,21 @@ def compare(gpu, ora, scores, L, rows=None, rel_tol=REL_TOL, gpu_scores=None):
                 exact += 1
             else:
                 s = np.asarray(scores[t][h], dtype=np.float64)
-                tol = rel_tol * (np.abs(s).max() if s.size else 0.0)
-                sg = s[ids]
-                so = s[o[:n]]
-                bad = np.abs(sg - so) > tol
-                assert not bad.any(), (
+                tol = _tol(s, rel_tol)
+                ok, gap = _rank_gaps(ids, o[:n], s, tol)
+                assert ok.all(), (
                     f"row {t} head {h}: gpu {g[:n]} vs oracle {o[:n]}; score gaps "
-                    f"{(sg - so)[bad]} exceed tol {tol}")
+                    f"{gap[~ok]} exceed tol {tol} (or NaN picks differ)")
             if gpu_scores is not None and Lt > 0:
                 s = np.asarray(scores[t][h], dtype=np.float64)
-                tol = rel_tol * np.abs(s).max()
+                tol = _tol(s, rel_tol)
                 gs = np.asarray(gpu_scores[t, h, :Lt], dtype=np.float64)
-                diff = np.abs(gs - s)
+                assert np.array_equal(np.isnan(gs), np.isnan(s)), (
+                    f"row {t} head {h}: NaN scores at {np.nonzero(np.isnan(gs))[0]} vs "
+                    f"oracle {np.nonzero(np.isnan(s))[0]}")
+                fin = ~np.isnan(s)
+                with np.errstate(invalid="ignore"):
+                    diff = np.where(gs[fin] == s[fin], 0.0, np.abs(gs[fin] - s[fin]))
                 assert np.all(diff <= tol), (
                     f"row {t} head {h}: score error {diff.max()} > tol {tol}")
     return exact / max(total, 1)
@@ -96,12 +121,13 @@ def compare_forced(gpu, ora, scores, L, topk, init_blocks, local_blocks, max_k_t
             om = np.array(sorted(set(o[o >= 0].tolist()) - forced))
             assert len(gm) == len(om)
             s = np.asarray(scores[t][h], dtype=np.float64)
-            tol = rel_tol * (np.abs(s).max() if s.size else 0.0)
-            sg = np.sort(s[gm])[::-1]
-            so = np.sort(s[om])[::-1]
-            bad = np.abs(sg - so) > tol
-            assert not bad.any(), (f"row {t} head {h}: gpu {g} vs oracle {o}; score gaps "
-                                   f"{(sg - so)[bad]} exceed tol {tol}")
+            tol = _tol(s, rel_tol)
+            # the chosen pages in selection order (score desc, NaN last, id asc)
+            key = lambda j: (np.isnan(s[j]), -s[j] if not np.isnan(s[j]) else 0.0, j)  # noqa: E731
+            ok, gap = _rank_gaps(np.array(sorted(gm, key=key), dtype=np.int64),
+                                 np.array(sorted(om, key=key), dtype=np.int64), s, tol)
+            assert ok.all(), (f"row {t} head {h}: gpu {g} vs oracle {o}; score gaps "
+                              f"{gap[~ok]} exceed tol {tol} (or NaN picks differ)")
     return exact / max(total, 1)
 
 

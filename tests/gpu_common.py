@@ -1,6 +1,10 @@
 """Helpers of the GPU tests: run a workload through the library and through
 the oracle."""
 
+import multiprocessing
+import os
+from concurrent.futures import ProcessPoolExecutor
+
 import numpy as np
 import torch
 
@@ -47,19 +51,20 @@ def run_gpu(w, dw=None, scale=1.0, budget=None, seq_lens_host_ub=None, scores=Fa
             None if sp is None else sp.cpu().numpy(), dw, step)
 
 
-def run_oracle(w, pool=None, scale=1.0):
+def run_oracle(w, pool=None, scale=1.0, max_pages=None):
     """Oracle outputs of the whole workload (small workloads only)."""
     if pool is None:
         pool = W.host_pool(w, oracle.write_pages)
     outs, scs, Ls = [], [], []
     if w.Rd:
         o, s, L = oracle.oracle_decode(w.q_codes[:w.n_decode_rows], pool, w.block_table[:w.Rd],
-                                       w.dec_seq_lens, w.query_len, scale, q_dtype=w.q_dtype)
+                                       w.dec_seq_lens, w.query_len, scale, q_dtype=w.q_dtype,
+                                       max_pages=max_pages)
         outs.append(o), scs.extend(s), Ls.append(L)
     if w.Rp:
         o, s, L = oracle.oracle_prefill(w.q_codes[w.n_decode_rows:], pool, w.block_table[w.Rd:],
                                         w.cu_seqlens_q, w.seq_lens[w.Rd:], w.pre_ctx, scale,
-                                        q_dtype=w.q_dtype)
+                                        q_dtype=w.q_dtype, max_pages=max_pages)
         outs.append(o), scs.extend(s), Ls.append(L)
     return np.concatenate(outs), scs, np.concatenate(Ls), pool
 
@@ -86,3 +91,45 @@ def oracle_request_rows(w, r, rows_in_req, scale=1.0):
     out, sc, L = oracle.index_rows(q, pos, kp, scale)
     scores = [sc[i, :, :max(int(L[i]), 0)] for i in range(len(rows_in_req))]
     return T0 + rows_in_req, out, scores, L
+
+
+def _one_thread_blas():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+
+
+def oracle_rows_parallel(w, jobs, workers=None):
+    """oracle_request_rows(w, r, rows) for every (r, rows) in ``jobs``, on CPU
+    worker processes (fresh interpreters started by spawn: they import only
+    numpy, the oracle and the generators, never touch the GPU and run one
+    BLAS thread each).  Returns the results in job order."""
+    if workers is None:
+        workers = min(12, len(os.sched_getaffinity(0)), max(len(jobs), 1))
+    ctx = multiprocessing.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx,
+                             initializer=_one_thread_blas) as ex:
+        futs = [ex.submit(oracle_request_rows, w, r, np.asarray(rows)) for r, rows in jobs]
+        return [f.result() for f in futs]
+
+
+def split_tiles(step):
+    """(request, first row, row count) of every tile the last prefill plan of
+    ``step`` split into page ranges, read from the pinned staging copy of the
+    plan (header word 6 = split tiles, word 7 = their word offset, 8 words
+    each)."""
+    k = step._next_staging ^ 1
+    st = step.pre_staging[k].numpy().view(np.int32)
+    n, off = int(st[6]), int(st[7])
+    return [tuple(int(x) for x in st[off + 8 * i:off + 8 * i + 3]) for i in range(n)]
+
+
+def decode_error_bits(step):
+    """Error word of the decode workspace (bit 0: invalid page id skipped,
+    bit 1: plan overflow, bit 2: rows refused past max_pages)."""
+    return int(step.dec_ws[:4].view(torch.int32).item())
+
+
+def prefill_error_bits(step):
+    """Error word of the prefill plan (int32 word 9; bit 0: invalid page id
+    skipped, bit 2: rows refused past max_pages)."""
+    return int(step.pre_plan[36:40].view(torch.int32).item())

@@ -17,6 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
+    # the indexer's ABI (the probe header is checked on its own below)
     txt = open(os.path.join(ROOT, "include", "mi_idx.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(mi_idx_[a-z_0-9]+)\s*\(", txt)))
@@ -28,9 +29,21 @@ def m():
     return m
 
 
+def test_probe_library_exports_its_header(m):
+    """libmi_idx_probe.so (the benchmark's HBM read-ceiling probes) exports
+    what include/mi_idx_probe.h declares."""
+    txt = open(os.path.join(ROOT, "include", "mi_idx_probe.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    names = sorted(set(re.findall(r"\b(mi_idx_probe_[a-z_0-9]+)\s*\(", txt)))
+    assert names == ["mi_idx_probe_read_pages", "mi_idx_probe_read_stream"]
+    raw = ctypes.CDLL(os.path.join(os.path.dirname(m.LIB_PATH), "libmi_idx_probe.so"))
+    for n in names:
+        assert hasattr(raw, n), n
+
+
 def test_library_exports_every_declared_symbol(m):
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     raw = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -58,6 +71,20 @@ def test_sizes(m):
                                                             + 8 * 512)
     assert m.mi_idx_prefill_plan_bytes(1, 10, 9) == 0
     assert m.mi_idx_prefill_workspace_bytes() == 1024 * 256 * 16 * 8
+
+
+def test_decode_plan_capacity(m):
+    """Work items of a decode plan: one per request plus the 2048 the scorer
+    holds at once; 64 header bytes + 16 bytes per item make the plan."""
+    for R in (0, 1, 64, 1000):
+        cap = m.mi_idx_decode_plan_capacity(R, 2048, 2, 4)
+        assert cap == R + 2048
+        assert m.mi_idx_decode_plan_bytes(R) == 64 + 16 * cap
+    assert m.mi_idx_decode_plan_capacity(-1, 10, 1, 1) == 0
+    assert m.mi_idx_decode_plan_capacity(4, -1, 1, 1) == 0
+    assert m.mi_idx_decode_plan_capacity(4, 10, 0, 1) == 0
+    assert m.mi_idx_decode_plan_capacity(4, 10, 9, 1) == 0
+    assert m.mi_idx_decode_plan_capacity(4, 10, 1, 9) == 0
 
 
 def _fake(n=1 << 20):

@@ -13,7 +13,8 @@ import torch
 import oracle
 import workloads as W
 from tests import checker, pins
-from tests.gpu_common import lib, oracle_request_rows, run_gpu, run_oracle
+from tests.gpu_common import (decode_error_bits, lib, oracle_rows_parallel, prefill_error_bits,
+                              run_gpu, run_oracle, split_tiles)
 from workloads.device import DeviceWorkload
 
 pytestmark = pytest.mark.gpu
@@ -89,7 +90,7 @@ def test_scale_and_repeat_invariance():
     for scale in (2.0, 0.125, 0.7):
         b, _, _, _, _ = run_gpu(w, dw=dw, scale=scale)
         assert np.array_equal(a, b), scale
-    # several layers on one plan (the arrival counters reset themselves)
+    # several layers scored on one plan
     c, _, _, _, _ = run_gpu(w, dw=dw, layers=3)
     assert np.array_equal(a, c)
 
@@ -162,7 +163,9 @@ def test_decode_replan_in_place():
         checker.compare(got, ref, scores, L)
 
 
-def test_zero_and_identical_queries():
+def test_zero_queries():
+    """All-zero queries: every page scores 0, so ids go in ascending order
+    (identical non-zero pages are tested in test_gpu_edges.py)."""
     _banner("zero queries")
     w = W.make_workload("decode_batch_small", 8)
     w.q_codes = np.zeros_like(w.q_codes)
@@ -183,7 +186,7 @@ def test_poisoned_block_table_tail_and_spare_pages_are_never_read():
     ref, scores, L, _ = run_oracle(w)
     checker.compare(out, ref, scores, L)
     # error word of the decode workspace: no invalid page id, no overflow
-    assert int(step.dec_ws[:4].view(torch.int32).item()) == 0
+    assert decode_error_bits(step) == 0
 
 
 def test_invalid_page_ids_inside_a_history_are_skipped():
@@ -220,32 +223,47 @@ def test_invalid_page_ids_inside_a_history_are_skipped():
     checker.compare(out, ref_mod, finite, L)
     for t in range(out.shape[0]):
         assert not set(bad_ids) & set(out[t, :, :15].ravel().tolist())
-    assert int(step.dec_ws[:4].view(torch.int32).item()) & 1 == 1
+    assert decode_error_bits(step) & 1 == 1
+    assert prefill_error_bits(step) & 1 == 1
 
 
-def _full_size(name):
+def _full_size(name, pick):
+    """Run a full-size workload in the benchmark's launch configuration; check
+    the contract invariants on every row, and compare the rows ``pick(w,
+    step)`` names -- a list of (request, rows of the request) -- with the
+    oracle, computed on CPU worker processes."""
     w = W.make_workload(name, 0)
     _banner(f"full-size {name}: T={w.T} pages={w.num_blocks}")
     out, _, _, dw, step = run_gpu(w)
-    req, pos = (oracle.rows_decode(w.dec_seq_lens, w.query_len) if w.Rd else
-                (np.zeros(0, int), np.zeros(0, int)))
     Ls = []
     if w.Rd:
+        _, pos = oracle.rows_decode(w.dec_seq_lens, w.query_len)
         Ls.append(np.where(pos >= 0, pos // 128, -1))
     if w.Rp:
         _, pp = oracle.rows_prefill(w.cu_seqlens_q, w.pre_ctx)
         Ls.append(pp // 128)
     L = np.concatenate(Ls)
     pins.check_invariants(out, L)
-    R = len(w.seq_lens)
-    picks = sorted(set([0, R // 2, R - 1]))
-    for r in picks:
-        nrows = w.query_len if r < w.Rd else int(w.pre_new[r - w.Rd])
-        sel = np.unique(np.concatenate([np.arange(min(nrows, 3)), [nrows - 1], np.arange(nrows)[::max(nrows // 9, 1)]]))
-        T, o, sc, Lr = oracle_request_rows(w, r, sel)
-        sub = out[T]
-        checker.compare(sub, o, sc, Lr)
+    jobs = pick(w, step)
+    _banner(f"full-size {name}: oracle on {sum(len(r) for _, r in jobs)} rows of "
+            f"{len(jobs)} requests")
+    compared = 0
+    for T, o, sc, Lr in oracle_rows_parallel(w, jobs):
+        checker.compare(out[T], o, sc, Lr)
+        compared += len(T)
+    _banner(f"full-size {name}: {compared} rows x {w.H} heads match the oracle")
     return w, out
+
+
+def _decode_requests(rs):
+    return lambda w, step: [(r, np.arange(w.query_len)) for r in rs]
+
+
+def _prefill_tile(w, r, tile):
+    """Rows of one whole row tile (256 / H rows) of prefill request r."""
+    M = 256 // w.H
+    n = int(w.pre_new[r - w.Rd])
+    return np.arange(tile * M, min(n, (tile + 1) * M))
 
 
 @pytest.mark.slow
@@ -258,12 +276,14 @@ def test_full_size_tiny_decode():
 
 @pytest.mark.slow
 def test_full_size_decode_batch():
-    _full_size("decode_batch")
+    """Every row of the 64-request decode batch."""
+    _full_size("decode_batch", _decode_requests(range(64)))
 
 
 @pytest.mark.slow
 def test_full_size_multi_token_decode():
-    w, out = _full_size("multi_token_decode")
+    """Every 8th request (16 of 128), all four query rows."""
+    w, out = _full_size("multi_token_decode", _decode_requests(range(0, 128, 8)))
     hits = total = 0
     for r in range(w.Rd):
         planted = set(w.planted_pages(r).tolist())
@@ -276,9 +296,29 @@ def test_full_size_multi_token_decode():
 
 @pytest.mark.slow
 def test_full_size_ragged_prefill():
-    _full_size("ragged_prefill")
+    """Every request: its last whole row tile (the longest histories) and one
+    row of each of its tiles the plan split into page ranges."""
+    def pick(w, step):
+        splits = split_tiles(step)
+        assert splits, "the ragged batch is expected to split tiles"
+        jobs = []
+        for r in range(w.Rd, len(w.seq_lens)):
+            n = int(w.pre_new[r - w.Rd])
+            rows = set(_prefill_tile(w, r, (n - 1) // (256 // w.H)).tolist())
+            rows |= {row0 + nrows // 2 for (rq, row0, nrows) in splits if rq == r - w.Rd}
+            jobs.append((r, np.array(sorted(rows))))
+        return jobs
+    _full_size("ragged_prefill", pick)
 
 
 @pytest.mark.slow
 def test_full_size_mixed_step():
-    _full_size("mixed_step")
+    """Every 4th decode request (8 of 32), both rows; a whole row tile of
+    each prefill request (the last of the first, a middle one of the
+    second)."""
+    def pick(w, step):
+        jobs = [(r, np.arange(w.query_len)) for r in range(0, w.Rd, 4)]
+        jobs.append((w.Rd, _prefill_tile(w, w.Rd, 8192 // 64 - 1)))
+        jobs.append((w.Rd + 1, _prefill_tile(w, w.Rd + 1, 64)))
+        return jobs
+    _full_size("mixed_step", pick)

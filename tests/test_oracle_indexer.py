@@ -162,6 +162,64 @@ def test_nan_scores_rank_last():
     assert oracle.select_row(s, 5).tolist()[:5] == [2, 0, 4, 1, 3]
 
 
+def test_nan_token_makes_page_nan_and_ranks_last():
+    """OCP MX v1.0: E8M0 byte 0xFF is NaN and makes every value of its 32-dim
+    block NaN; a dot product with a NaN term is NaN whatever query element
+    meets it (0 x NaN is NaN in IEEE 754); the page max propagates it and NaN
+    pages rank after every number, among themselves by lower id."""
+    rng = np.random.default_rng(21)
+    clean = _random_case(rng, 12, dup=False).reshape(12, 128, 68)
+    pool = clean.copy()
+    pool[5, 17, 64] = 0xFF          # block 0 of a token of physical page 5
+    pool[8, 100, 67] = 0xFF         # block 3 of a token of physical page 8
+    bt = np.array([np.arange(12)[::-1]], dtype=np.int32)      # logical j -> physical 11-j
+    q = np.zeros((1, 1, 128), dtype=np.uint8)
+    q[0, 0, 40] = 0x38               # one-hot on dim 40 (block 1): NaN blocks meet zeros
+    seq = np.array([11 * 128 + 3], dtype=np.int32)            # history 0..10
+    out, scores, L = oracle.oracle_decode(q, pool.reshape(12, 8704), bt, seq, 1)
+    nan_logical = {11 - 5, 11 - 8}
+    s = scores[0][0]
+    assert set(np.nonzero(np.isnan(s))[0].tolist()) == nan_logical
+    _, ex = pins.Exact().run(q, clean.reshape(12, 8704), bt, [0], [int(seq[0]) - 1], 1.0)
+    finite = sorted((j for j in range(11) if j not in nan_logical),
+                    key=lambda j: (-ex[(0, 0)][j], j))
+    assert out[0, 0].tolist() == finite + sorted(nan_logical) + [-1] * 4 + [11]
+
+
+def test_nan_query_element_makes_every_page_nan():
+    """An E4M3 NaN byte (0x7F / 0xFF) in the query makes every dot product,
+    hence every page score, NaN: all pages tie and go in id order."""
+    rng = np.random.default_rng(22)
+    pool = _random_case(rng, 30, dup=False)
+    bt = np.array([np.arange(30)], dtype=np.int32)
+    for code in (0x7F, 0xFF):
+        q = _random_q(rng, (1, 1, 128))
+        q[0, 0, 77] = code
+        out, scores, _ = oracle.oracle_decode(q, pool, bt, np.array([25 * 128 + 1]), 1)
+        assert np.all(np.isnan(scores[0][0]))
+        assert out[0, 0].tolist() == list(range(15)) + [25]
+
+
+def test_rows_past_max_pages_are_refused():
+    """A row whose history needs block-table column max_pages or later is
+    refused (all 16 slots -1, L = -1); a row whose history ends exactly at
+    max_pages columns is served as without the bound."""
+    w = W.make_workload("edge_short", 0)
+    pool = W.host_pool(w, oracle.write_pages)
+    base, _, Lb = oracle.oracle_decode(w.q_codes, pool, w.block_table, w.dec_seq_lens,
+                                       w.query_len)
+    mp = 2
+    out, _, L = oracle.oracle_decode(w.q_codes, pool, w.block_table, w.dec_seq_lens,
+                                     w.query_len, max_pages=mp)
+    _, pos = oracle.rows_decode(w.dec_seq_lens, w.query_len)
+    for t in range(len(pos)):
+        if pos[t] >= 0 and pos[t] // 128 > mp:
+            assert L[t] == -1 and np.all(out[t] == -1), t
+        else:
+            assert L[t] == Lb[t] and np.array_equal(out[t], base[t]), t
+    assert (L == -1).sum() > (Lb == -1).sum() and (Lb == mp).any()
+
+
 def test_heap_selection_agrees():
     rng = np.random.default_rng(12)
     for L in [0, 1, 7, 15, 16, 40, 300]:

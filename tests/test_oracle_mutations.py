@@ -33,6 +33,9 @@ PINS = [
     TI.test_identical_pages_tie_to_lower_id,
     TI.test_heap_selection_agrees,
     TI.test_nan_scores_rank_last,
+    TI.test_nan_token_makes_page_nan_and_ranks_last,
+    TI.test_nan_query_element_makes_every_page_nan,
+    TI.test_rows_past_max_pages_are_refused,
     TI.test_prefill_row_equals_decode_row_at_same_position,
     TP.test_chunks_against_bruteforce_and_properties,
     TFO.test_bruteforce_tiny_rows,
@@ -136,6 +139,25 @@ def _page_scores_sum(q, kpages):
 
 
 _orig_rows_decode = I.rows_decode
+
+
+def _page_scores_nanmax(q, kpages):
+    q = np.asarray(q, dtype=np.float64).reshape(-1, 128)
+    J = kpages.shape[0]
+    if J == 0:
+        return np.zeros((q.shape[0], 0))
+    dots = (q @ kpages.reshape(J * 128, 128).T).reshape(q.shape[0], J, 128)
+    with np.errstate(all="ignore"):
+        m = np.where(np.isnan(dots), -np.inf, dots).max(axis=2)
+    return m
+
+
+_orig_local_pages = I.local_pages
+
+
+def _local_pages_clamped(positions, max_pages=None):
+    L = _orig_local_pages(positions)
+    return L if max_pages is None else np.minimum(L, max_pages)
 
 
 def _rows_decode_shifted(seq_lens, query_len):
@@ -260,6 +282,8 @@ MUTATIONS = {
     "nan_ranks_first": [(I, "select_row", _select_nan_first), (oracle, "select_row", _select_nan_first)],
     "local_leaks": [(I, "select_row", _select_local_in_history)],
     "sum_not_max": [(I, "page_scores", _page_scores_sum)],
+    "page_max_drops_nan": [(I, "page_scores", _page_scores_nanmax)],
+    "rows_past_max_pages_clamped": [(I, "local_pages", _local_pages_clamped)],
     "decode_positions_shifted": [(I, "rows_decode", _rows_decode_shifted),
                                  (oracle, "rows_decode", _rows_decode_shifted)],
     "prefill_positions_shifted": [(I, "rows_prefill", _rows_prefill_off_by_one),
