@@ -35,6 +35,8 @@ _SIGS = {
     "mi_idx_insert_mxfp4": (_i32, [_vp, _i32, _i64, _vp, _i64, _vp, _i64, _vp]),
     "mi_idx_decode_plan_bytes": (_sz, [_i32]),
     "mi_idx_decode_plan_capacity": (_sz, [_i32, _i32, _i32, _i32]),
+    "mi_idx_decode_noalloc": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
+                                     _i32, _f32, _vp, _vp, _vp]),
     "mi_idx_decode_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "mi_idx_plan_decode": (_i32, [_vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp, _sz, _vp]),
     "mi_idx_score_topk_decode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
@@ -61,6 +63,7 @@ PAGE_BYTES = 8704
 TOPK = 16
 MAX_QUERY_LEN = 8
 MAX_HEADS = 8
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 OK, EINVAL, EUNSUPPORTED, ECAPACITY, EHIP = 0, 1, 2, 3, 4
 
@@ -233,6 +236,21 @@ def _decode_args(q, pages, block_table, seq_lens, query_len, max_pages, topk_out
         if tuple(scores_out.shape) != (R * query_len, H, max_pages):
             raise ValueError("scores_out must be [rows, H, max_pages]")
     return R, H
+
+
+def mi_idx_decode_noalloc(q, pages, block_table, seq_lens, query_len, max_pages, topk_out,
+                          scale=1.0, scores_out=None, stream=None):
+    """Plan + score + merge of the decode rows with the library's static
+    device scratch (no plan or workspace, nothing allocated); the same
+    arguments and result as mi_idx_plan_decode + mi_idx_score_topk_decode.
+    Calls that overlap on one GPU race."""
+    R, H = _decode_args(q, pages, block_table, seq_lens, query_len, max_pages, topk_out,
+                        scores_out)
+    st = lib.mi_idx_decode_noalloc(
+        _ptr(q), _q_dtype(q), _ptr(pages), pages.numel() // PAGE_BYTES, _ptr(block_table),
+        block_table.stride(0), _ptr(seq_lens), R, query_len, H, max_pages, float(scale),
+        _ptr(topk_out), _ptr(scores_out), _stream(stream))
+    _check(st, "mi_idx_decode_noalloc")
 
 
 def mi_idx_prefill_plan_bytes(num_reqs, total_q, num_heads):

@@ -22,6 +22,7 @@
 // merges the request's item lists into the 16 output slots of every row.
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 
@@ -690,4 +691,77 @@ extern "C" int mi_idx_score_topk_decode(const void *q, int q_dtype, const uint8_
                       bt_stride, seq_lens, num_reqs, query_len, num_heads, max_pages, scale,
                       (const int32_t *)plan, plan_capacity(plan_bytes), (uint8_t *)workspace,
                       topk_out, scores_out, (hipStream_t)stream);
+}
+
+// ------------------------------------------------------- allocation-free --
+// Plan + score + merge with the plan and the workspace in one file-scope
+// device array instead of caller buffers.  Host code never passes the
+// array's name to a kernel (in host code it is a host-side stand-in, not a
+// device address): the device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+static __device__ __align__(256) uint8_t scratch[MI_IDX_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[64];
+
+static int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return mi_idx_fail(MI_IDX_EHIP, "decode_noalloc: no current device: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= 64)
+    return mi_idx_fail(MI_IDX_EUNSUPPORTED, "decode_noalloc: device %d beyond the 64 served", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return mi_idx_fail(MI_IDX_EHIP, "decode_noalloc: hipGetSymbolAddress failed: %s",
+                         hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MI_IDX_OK;
+}
+
+extern "C" int mi_idx_decode_noalloc(const void *q, int q_dtype, const uint8_t *pages,
+                                     int64_t num_blocks, const int32_t *block_table,
+                                     int64_t bt_stride, const int32_t *seq_lens, int num_reqs,
+                                     int query_len, int num_heads, int max_pages, float scale,
+                                     int32_t *topk_out, float *scores_out, void *stream) {
+  mi_idx_clear_error();
+  if (num_reqs < 0) return mi_idx_fail(MI_IDX_EINVAL, "decode_noalloc: num_reqs %d < 0", num_reqs);
+  if (query_len < 1 || query_len > MI_IDX_MAX_QUERY_LEN)
+    return mi_idx_fail(MI_IDX_EUNSUPPORTED, "decode_noalloc: query_len %d outside 1..8", query_len);
+  if (num_heads < 1 || num_heads > MI_IDX_MAX_HEADS)
+    return mi_idx_fail(MI_IDX_EUNSUPPORTED, "decode_noalloc: num_heads %d outside 1..8", num_heads);
+  if (max_pages < 0) return mi_idx_fail(MI_IDX_EINVAL, "decode_noalloc: max_pages %d < 0", max_pages);
+  const size_t plan_bytes = mi_idx_decode_plan_bytes(num_reqs);
+  const size_t plan_region = (plan_bytes + 255) & ~(size_t)255;
+  const size_t ws_bytes = mi_idx_decode_workspace_bytes(num_reqs, query_len, num_heads);
+  if (plan_region + ws_bytes > (size_t)MI_IDX_NOALLOC_SCRATCH_BYTES)
+    return mi_idx_fail(MI_IDX_ECAPACITY, "decode_noalloc: %d requests x %d query columns need "
+                       "%zu scratch bytes, above the %d-byte static scratch", num_reqs,
+                       query_len * num_heads, plan_region + ws_bytes,
+                       MI_IDX_NOALLOC_SCRATCH_BYTES);
+  int st = check_score_args("decode_noalloc", q, q_dtype, pages, num_blocks, block_table,
+                            bt_stride, seq_lens, max_pages, scale, topk_out);
+  if (st) return st;
+  if (num_reqs == 0) return MI_IDX_OK;
+  void *base = nullptr;
+  st = scratch_address(&base);
+  if (st) return st;
+  int32_t *plan = static_cast<int32_t *>(base);
+  uint8_t *ws = static_cast<uint8_t *>(base) + plan_region;
+  const int cap = plan_capacity(plan_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  st = launch_plan(seq_lens, num_reqs, query_len, num_heads, max_pages, plan, cap, ws, s);
+  if (st) return st;
+  return launch_score(static_cast<const uint8_t *>(q), q_dtype, pages, num_blocks, block_table,
+                      bt_stride, seq_lens, num_reqs, query_len, num_heads, max_pages, scale, plan,
+                      cap, ws, topk_out, scores_out, s);
 }

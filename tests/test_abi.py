@@ -43,7 +43,7 @@ def test_probe_library_exports_its_header(m):
 
 def test_library_exports_every_declared_symbol(m):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     raw = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -85,6 +85,36 @@ def test_decode_plan_capacity(m):
     assert m.mi_idx_decode_plan_capacity(4, 10, 0, 1) == 0
     assert m.mi_idx_decode_plan_capacity(4, 10, 9, 1) == 0
     assert m.mi_idx_decode_plan_capacity(4, 10, 1, 9) == 0
+
+
+def test_decode_noalloc_argument_errors(m):
+    """The allocation-free decode call rejects what the caller-buffer calls
+    reject, and inputs whose plan + workspace exceed its static scratch,
+    before touching any device memory."""
+    L = m.lib
+    buf = _fake().ctypes.data
+
+    def call(R=4, ql=2, H=2, mp=16, sc=1.0, qd=0, q=buf, out=buf, bts=16, nb=10):
+        return L.mi_idx_decode_noalloc(q, qd, buf, nb, buf, bts, buf, R, ql, H, mp, sc, out,
+                                       None, None)
+    assert call(ql=9) == m.EUNSUPPORTED
+    assert call(H=0) == m.EUNSUPPORTED
+    assert call(R=-1) == m.EINVAL
+    assert call(mp=-1) == m.EINVAL
+    assert call(sc=0.0) == m.EINVAL
+    assert call(qd=3) == m.EINVAL
+    assert call(q=None) == m.EINVAL
+    assert call(out=buf + 4) == m.EINVAL
+    assert call(bts=8) == m.EINVAL
+    assert call(nb=0) == m.EINVAL
+    # plan (rounded to 256) + workspace against the 32 MiB scratch
+    need = lambda R, ql, H: (-(-m.mi_idx_decode_plan_bytes(R) // 256) * 256  # noqa: E731
+                             + m.mi_idx_decode_workspace_bytes(R, ql, H))
+    assert need(512, 8, 8) <= m.NOALLOC_SCRATCH_BYTES
+    big = next(R for R in range(512, 1 << 16, 64) if need(R, 8, 8) > m.NOALLOC_SCRATCH_BYTES)
+    assert call(R=big, ql=8, H=8) == m.ECAPACITY
+    assert b"scratch" in L.mi_idx_last_error()
+    assert call(R=0) == m.OK
 
 
 def _fake(n=1 << 20):
