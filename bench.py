@@ -35,9 +35,14 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    # The GPU needs ~0.1 s of sustained work to reach its steady clocks; with
-    # only a few warmup steps the timed steps run ~10 % slow.
+    # Warm-up runs at least this many untimed steps and in any case until
+    # --warmup-seconds of back-to-back GPU work have passed: the GPU needs
+    # ~0.1 s of sustained work to reach its steady clocks (with only a few
+    # warm-up steps the timed steps ran ~10 % slow).
     p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--warmup-seconds", type=float, default=0.25)
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the HBM read-ceiling probes (libmi_idx_probe.so)")
     p.add_argument("--workload", default="mixed_step")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--pool-copies", type=int, default=None,
@@ -146,16 +151,75 @@ def measured_traffic(kernels, source, workload="mixed_step"):
     return int(sum(found.values()))
 
 
+def hbm_ceilings(torch, reps=5):
+    """Read ceilings of this GPU's HBM, for the decode phase to be reported
+    against next to the 8 TB/s figure: a coalesced read of a 2 GiB buffer,
+    and whole 8704-byte pages of a 1 GiB pool read in a random order (the
+    decode's access pattern) with 2 pages per wave and with 28 (the decode
+    plan's item length on the mixed step).  Median of ``reps`` launches
+    each, HIP events on the launching stream."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_block_mxfp4_amd",
+                                   "libmi_idx_probe.so"))
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.mi_idx_probe_read_stream.argtypes = [vp, i64, ctypes.c_int, vp, i64, vp]
+    lib.mi_idx_probe_read_pages.argtypes = [vp, i64, vp, i64, ctypes.c_int, vp, i64, vp]
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1 << 22, dtype=torch.int32, device="cuda")
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device="cuda")
+    npages = (1 << 30) // 8704
+    pool = buf[:npages * 8704]
+    order = torch.from_numpy(np.random.default_rng(0).permutation(npages).astype(np.int32)).cuda()
+
+    def timed(call, nbytes):
+        call()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = call()
+            e1.record(stream)
+            if st != 0:
+                raise RuntimeError(f"probe failed with status {st}")
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+        return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+    s = stream.cuda_stream
+    # 8 workgroups per CU: within 1 % of the best of 1..16 on a 1-4 GiB sweep
+    out = {"read_stream_GBps": timed(lambda: lib.mi_idx_probe_read_stream(
+        buf.data_ptr(), buf.numel(), 8, sink.data_ptr(), sink.numel(), s), buf.numel())}
+    for per_wave in (2, 28):
+        out[f"random_pages_{per_wave}_per_wave_GBps"] = timed(
+            lambda: lib.mi_idx_probe_read_pages(pool.data_ptr(), npages, order.data_ptr(),
+                                                npages, per_wave, sink.data_ptr(), sink.numel(),
+                                                s), npages * 8704)
+    out["spec_GBps"] = PEAK_HBM_GBPS
+    out["bytes"] = {"read_stream": int(buf.numel()), "random_pages": int(npages * 8704)}
+    del buf, pool, order, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, budget_s):
     """The oracle on a bounded sample of the step: whole decode requests
     (scoring + selection) until about a third of the time budget is spent,
     then blocks of 256 rows of the first prefill request until the rest is;
     pages are encoded before the clock starts.  Extrapolated to the step by
-    counts of requests and rows."""
+    counts of requests and rows.  BLAS runs one thread per core this process
+    may use (its CPU affinity)."""
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(cores):
+        return _cpu_baseline(w, budget_s, cores)
+
+
+def _cpu_baseline(w, budget_s, cores):
     import oracle
     from threadpoolctl import threadpool_info
 
-    cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
 
     def request_pages(r):
         k = w.k_rows(r)
@@ -207,17 +271,30 @@ def cpu_baseline(w, budget_s):
             "kind": "oracle", "sample": "; ".join(parts) +
             f"; {sample_s:.1f} s of oracle time, extrapolated to the step by request and row "
             f"counts (est. {est:.1f} s per step)",
-            "cpu": _cpu_model()}
+            "blas_threads": int(blas_threads), "affinity_cpus": int(cores),
+            "host_cpus": os.cpu_count(), "cpu": _cpu_model()}
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it (model, family/model/stepping,
+    MHz)."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (x.strip() for x in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping", "cpu MHz") and \
+                        k not in info:
+                    info[k] = v
+            if not line.strip() and info:
+                break
     except OSError:
         pass
-    return "unknown"
+    if not info:
+        return "unknown"
+    return (f"{info.get('model name', 'unknown')} (family {info.get('cpu family', '?')}, "
+            f"model {info.get('model', '?')}, stepping {info.get('stepping', '?')}, "
+            f"{info.get('cpu MHz', '?')} MHz)")
 
 
 KERNEL_SOURCES = {"decode_plan_kernel": "decode.hip", "decode_score_kernel": "decode.hip",
@@ -381,10 +458,18 @@ def main():
             e[3].record(stream)
             ev.append(e)
 
-    for i in range(a.warmup):
-        one_step(i, False)
+    tw = time.perf_counter()
+    nwarm = 0
+    while nwarm < a.warmup or time.perf_counter() - tw < a.warmup_seconds:
+        for _ in range(10 if nwarm >= a.warmup else 1):
+            one_step(nwarm, False)
+            nwarm += 1
+        if nwarm >= a.warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done; timing {a.steps} steps", file=sys.stderr, flush=True)
+    warm_s = time.perf_counter() - tw
+    print(f"[bench] warmup done ({nwarm} steps, {warm_s:.2f} s); timing {a.steps} steps",
+          file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(a.steps):
         one_step(i, True)
@@ -437,6 +522,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        "warmup_run": {"steps": nwarm, "seconds": round(warm_s, 3)},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -503,6 +589,14 @@ def main():
             "algorithmic_bytes": sel_bytes,
             "GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    if not a.no_ceiling:
+        print("[bench] HBM read ceilings", file=sys.stderr, flush=True)
+        ceil = hbm_ceilings(torch)
+        res["hbm_ceiling"] = ceil
+        if w.Rd:
+            roof_dec["frac_of_read_stream"] = round(dec_gbps / ceil["read_stream_GBps"], 4)
+            roof_dec["frac_of_random_pages"] = round(
+                dec_gbps / ceil["random_pages_2_per_wave_GBps"], 4)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

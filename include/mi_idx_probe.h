@@ -20,11 +20,12 @@ extern "C" {
 #endif
 
 /* Reads the `bytes` bytes at `buf` (16-byte aligned; bytes rounded down to a
- * multiple of 16) once, as coalesced 16-byte loads, with 8 workgroups of 256
- * threads per compute unit.  sink: >= 2048 * CUs uint32 words of scratch the
- * kernel practically never writes. */
-int mi_idx_probe_read_stream(const void *buf, int64_t bytes, uint32_t *sink,
-                             int64_t sink_words, void *stream);
+ * multiple of 16) once, as coalesced 16-byte loads: blocks_per_cu (1..64)
+ * workgroups of 256 threads per compute unit take 32 KB chunks in turn, 8
+ * loads per thread in flight.  sink: >= 256 * blocks_per_cu * CUs uint32
+ * words of scratch the kernel practically never writes. */
+int mi_idx_probe_read_stream(const void *buf, int64_t bytes, int blocks_per_cu,
+                             uint32_t *sink, int64_t sink_words, void *stream);
 
 /* Reads n_order whole 8704-byte pages of `pages` ([num_pages, 8704], 16-byte
  * aligned) in the order of `order` (int32 page ids; an id outside

@@ -18,7 +18,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmi_idx.so")
+# MI_IDX_LIB selects another build of the same library (the sanitizer build
+# of build.py --sanitize-check); by default the in-tree libmi_idx.so.
+LIB_PATH = os.environ.get("MI_IDX_LIB") or os.path.join(_HERE, "libmi_idx.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is not built; run `python sparse_attention_block_mxfp4_amd/build.py` "

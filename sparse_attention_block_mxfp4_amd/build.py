@@ -69,6 +69,40 @@ def _build_lib(sources, lib, verbose, extra):
     return lib
 
 
+# Host-code sanitizer build (CPU checks of the argument validation and the
+# prefill planning): AddressSanitizer + UndefinedBehaviorSanitizer on the
+# host pass only; device code is compiled as usual.
+SANITIZE_FLAGS = "-Xarch_host -fsanitize=address,undefined -Xarch_host -fno-omit-frame-pointer " \
+                 "-Xarch_host -g".split()
+SANITIZE_DIR = os.path.join(HERE, "_sanitize")
+
+
+def asan_runtime():
+    """The ASan runtime of hipcc's clang, to preload into the test process."""
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found under /opt/rocm/llvm")
+    return found[-1]
+
+
+def sanitize_check(verbose=False):
+    """Build libmi_idx.so with sanitized host code into _sanitize/ and run the
+    CPU ABI tests (argument errors, prefill planning) against it with the
+    ASan runtime preloaded; returns pytest's exit status."""
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    lib = os.path.join(SANITIZE_DIR, "libmi_idx.so")
+    _build_lib(SOURCES, lib, verbose, SANITIZE_FLAGS)
+    env = dict(os.environ, LD_PRELOAD=asan_runtime(), MI_IDX_LIB=lib,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    cmd = [sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider",
+           os.path.join(ROOT, "tests", "test_abi.py")]
+    print(" ".join(f"{k}={env[k]}" for k in ("LD_PRELOAD", "MI_IDX_LIB", "ASAN_OPTIONS",
+                                              "UBSAN_OPTIONS")), " ".join(cmd), flush=True)
+    return subprocess.run(cmd, env=env, cwd=ROOT).returncode
+
+
 def build(verbose=False, extra=()):
     """Compile every source (one object each, with its own flags) and link
     them into libmi_idx.so, and the probes into libmi_idx_probe.so; a library
@@ -79,4 +113,6 @@ def build(verbose=False, extra=()):
 
 
 if __name__ == "__main__":
+    if "--sanitize-check" in sys.argv:
+        sys.exit(sanitize_check(verbose=True))
     print(build(verbose=True))

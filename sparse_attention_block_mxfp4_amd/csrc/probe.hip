@@ -26,20 +26,25 @@ constexpr int kPageBytes = 8704;
 constexpr int kPageChunks = kPageBytes / 16;                // 544
 constexpr int kChunksPerLane = (kPageChunks + 63) / 64;     // 9 (the last partial)
 
+// Workgroup b reads 32 KB chunks b, b + grid, ...: load u of thread t takes
+// 16 bytes at chunk + 16 (256 u + t), so each load instruction of the
+// workgroup covers 4 KB of consecutive addresses.
 __global__ __launch_bounds__(kThreads) void read_stream_kernel(const u32x4 *__restrict__ buf,
                                                                int64_t n16, uint32_t never,
                                                                uint32_t *__restrict__ sink) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;   // 16-byte units per chunk
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+  const int64_t full = n16 / kChunk;
+  for (int64_t c = blockIdx.x; c < full; c += gridDim.x) {
+    const u32x4 *p = buf + c * kChunk + threadIdx.x;
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) v[u] = p[u * kThreads];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (int64_t i = full * kChunk + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kThreads) {
     const u32x4 v = buf[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
@@ -84,16 +89,18 @@ __global__ __launch_bounds__(kThreads) void read_pages_kernel(const uint8_t *__r
 
 }  // namespace
 
-extern "C" int mi_idx_probe_read_stream(const void *buf, int64_t bytes, uint32_t *sink,
-                                        int64_t sink_words, void *stream) {
-  if (!buf || !sink || bytes < 16 || ((uintptr_t)buf % 16) || ((uintptr_t)sink % 4)) return 1;
+extern "C" int mi_idx_probe_read_stream(const void *buf, int64_t bytes, int blocks_per_cu,
+                                        uint32_t *sink, int64_t sink_words, void *stream) {
+  if (!buf || !sink || bytes < 16 || ((uintptr_t)buf % 16) || ((uintptr_t)sink % 4) ||
+      blocks_per_cu < 1 || blocks_per_cu > 64)
+    return 1;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
     (void)hipGetLastError();
     return 4;
   }
-  const int64_t blocks = (int64_t)cus * 8;
+  const int64_t blocks = (int64_t)cus * blocks_per_cu;
   if (sink_words < blocks * kThreads) return 3;
   hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                      (hipStream_t)stream, static_cast<const u32x4 *>(buf), bytes / 16,

@@ -36,7 +36,7 @@ def test_probe_library_exports_its_header(m):
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     names = sorted(set(re.findall(r"\b(mi_idx_probe_[a-z_0-9]+)\s*\(", txt)))
     assert names == ["mi_idx_probe_read_pages", "mi_idx_probe_read_stream"]
-    raw = ctypes.CDLL(os.path.join(os.path.dirname(m.LIB_PATH), "libmi_idx_probe.so"))
+    raw = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "libmi_idx_probe.so"))
     for n in names:
         assert hasattr(raw, n), n
 
@@ -385,3 +385,29 @@ def test_prefill_equal_tiles_stay_whole(m):
     words, n, ch, mg = _plan_host(m, cu, sl, 4, 0)
     _check_plan(words, n, ch, mg, cu, sl, 4, 0)
     assert n == 256 and mg == 0
+
+
+def test_prefill_plan_adversarial_shapes(m):
+    """Host planning on shapes far from the workloads (the ones the heap
+    rebalancing and the offset arithmetic see least): thousands of tiny
+    requests, one request of many more tiles than work lists, contexts near a
+    billion tokens, empty requests between others and an all-empty batch."""
+    rng = np.random.default_rng(44)
+    cases = []
+    qn = rng.integers(0, 6, size=2000).astype(np.int32)
+    cases.append((qn, rng.integers(0, 10 ** 6, size=2000).astype(np.int32), 1, 0))
+    cases.append((np.array([200000, 3, 0, 7], dtype=np.int32),
+                  np.array([0, 50, 10 ** 5, 1], dtype=np.int32), 1, 0))
+    cases.append((np.array([1, 300, 1], dtype=np.int32),
+                  np.array([10 ** 9, 5000, 3], dtype=np.int32), 4, 64))
+    cases.append((np.array([0, 0, 0], dtype=np.int32), np.array([5, 0, 9], dtype=np.int32), 2, 0))
+    cases.append((np.array([8192] * 16, dtype=np.int32),
+                  np.array([131072] * 8 + [0] * 8, dtype=np.int32), 8, 100))
+    for qn, ctx, H, budget in cases:
+        sl = np.maximum(ctx + qn, 1).astype(np.int32)
+        cu = np.concatenate([[0], np.cumsum(qn)]).astype(np.int32)
+        words, n, ch, mg = _plan_host(m, cu, sl, H, budget)
+        if cu[-1] == 0:
+            assert n == 0 and words[4] == 0
+            continue
+        _check_plan(words, n, ch, mg, cu, sl, H, budget)
