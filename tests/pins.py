@@ -94,9 +94,10 @@ class Exact:
             out.append(self.e2m1[nib] * self.e8m0[int(page[base + 64 + d // 32])])
         return out
 
-    def page_score(self, page, q):
+    def page_score(self, page, q, ntok=128):
+        """max over tokens t < ntok of q . k_t, exactly."""
         best = None
-        for t in range(128):
+        for t in range(ntok):
             k = self.token(page, t)
             s = sum((qa * kb for qa, kb in zip(q, k)), Fraction(0))
             best = s if best is None or s > best else best

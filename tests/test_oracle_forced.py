@@ -12,11 +12,12 @@ import pytest
 import oracle
 
 
-def _brute(scores, L, topk, init_blocks, local_blocks, max_k_tiles):
+def _brute(scores, L, topk, init_blocks, local_blocks, max_k_tiles, local_score=None):
     """Every subset of the row's valid pages of the right size that holds the
     forced pages; the winner's non-forced part is the best when its members
     are listed best first (score descending, NaN last, lower id first on a
-    tie) and compared entry by entry."""
+    tie) and compared entry by entry.  The local page, when it competes,
+    carries ``local_score``."""
     if L < 0:
         return [-1] * topk
     nvp = L + 1
@@ -26,9 +27,10 @@ def _brute(scores, L, topk, init_blocks, local_blocks, max_k_tiles):
     fe = min(local_blocks, topk - fb)
     forced = set(range(fb)) | set(range(nvp - fe, nvp))
     rest = [j for j in range(nvp) if j not in forced]
+    full = list(scores[:L]) + [local_score]
 
     def rank(j):
-        s = scores[j]
+        s = full[j]
         return (1, 0.0, j) if np.isnan(s) else (0, -s, j)
     best = None
     for sub in itertools.combinations(rest, topk - len(forced)):
@@ -53,6 +55,48 @@ def test_bruteforce_tiny_rows():
         got = oracle.select_forced_row(s, L, topk, init, local, mkt)
         want = _brute(s, L, topk, init, local, mkt)
         assert list(got) == want, (s, L, topk, init, local, mkt, got, want)
+
+
+def test_bruteforce_tiny_rows_local_page_competing():
+    """No trailing window (local_blocks = 0, or init_blocks >= topk): the
+    local page competes on its causal-prefix score; topk beyond 16 too."""
+    rng = np.random.default_rng(15)
+    for _ in range(600):
+        L = int(rng.integers(-1, 11))
+        topk = int(rng.integers(1, 8))
+        init = int(rng.integers(0, 5))
+        local = int(rng.integers(0, 3))
+        mkt = int(rng.integers(0, 12))
+        s = rng.integers(0, 4, size=max(L, 0)).astype(np.float64)
+        if L > 0 and rng.random() < 0.2:
+            s[rng.integers(0, L)] = np.nan
+        ls = float(rng.integers(0, 4)) if rng.random() > 0.1 else np.nan
+        got = oracle.select_forced_row(s, L, topk, init, local, mkt, local_score=ls)
+        want = _brute(s, L, topk, init, local, mkt, local_score=ls)
+        assert list(got) == want, (s, L, topk, init, local, mkt, ls, got, want)
+    # a large topk over a long row: the forced windows and the best pages
+    s = rng.standard_normal(300)
+    got = oracle.select_forced_row(s, 300, 64, 3, 0, 10 ** 6, local_score=10.0)
+    order = [j for j in np.argsort(-s, kind="stable") if j >= 3][:60]
+    assert list(got) == sorted([0, 1, 2, 300] + order)
+
+
+def test_local_page_competes_special_cases():
+    s = np.array([5.0, 1.0, 4.0, 2.0, 3.0, 0.0, 6.0, 7.0])      # history 0..7, L = 8
+    # a high local score takes a slot, a low one does not
+    assert list(oracle.select_forced_row(s, 8, 4, 0, 0, 9, local_score=6.5)) == [0, 6, 7, 8]
+    assert list(oracle.select_forced_row(s, 8, 4, 0, 0, 9, local_score=0.5)) == [0, 2, 6, 7]
+    # a tie with a history page at the last slot goes to the lower id (page 6)
+    assert list(oracle.select_forced_row(s, 8, 2, 0, 0, 9, local_score=6.0)) == [6, 7]
+    assert list(oracle.select_forced_row(s, 8, 3, 0, 0, 9, local_score=6.0)) == [6, 7, 8]
+    # NaN ranks last
+    assert list(oracle.select_forced_row(s, 8, 4, 1, 0, 9, local_score=np.nan)) == [0, 2, 6, 7]
+    # init_blocks >= topk leaves no trailing window either: leading pages only
+    assert list(oracle.select_forced_row(s, 8, 4, 9, 1, 9, local_score=None)) == [0, 1, 2, 3]
+    # the local score is demanded exactly when the local page competes
+    with pytest.raises(ValueError):
+        oracle.select_forced_row(s, 8, 4, 0, 0, 9)
+    assert list(oracle.select_forced_row(s[:3], 3, 4, 0, 0, 9)) == [0, 1, 2, 3]
 
 
 def test_default_configuration_selects_the_sixteen_slot_set():
@@ -106,6 +150,6 @@ def test_output_form():
 
 def test_rejects_unserved_configurations():
     with pytest.raises(ValueError):
-        oracle.select_forced_row(np.zeros(4), 4, 4, 0, 0, 9)    # local page unforced
+        oracle.select_forced_row(np.zeros(4), 4, 4, 0, -1, 9)
     with pytest.raises(ValueError):
         oracle.select_forced_row(np.zeros(4), 4, 0, 0, 1, 9)

@@ -220,6 +220,45 @@ def test_rows_past_max_pages_are_refused():
     assert (L == -1).sum() > (Lb == -1).sum() and (Lb == mp).any()
 
 
+def test_local_page_scores_exact_bruteforce():
+    """Causal local-page scores against exact rationals over tokens
+    0 .. p % 128 of the row's own page (FlashInfer page, forward: causal)."""
+    rng = np.random.default_rng(31)
+    pool = _random_case(rng, 5, dup=False)
+    bt = np.array([[3, 1, 4, 0, 2], [2, 0, 1, 3, 4]], dtype=np.int32)
+    positions = [0, 1, 127, 128, 200, 255, 300, 511, 522]
+    req = [i % 2 for i in range(len(positions))]
+    q = _random_q(rng, (len(positions), 2, 128))
+    got = oracle.oracle_local_scores(q, pool, bt, req, positions, scale=0.5)
+    ex = pins.Exact()
+    for t, p in enumerate(positions):
+        page = pool[bt[req[t]][p // 128]]
+        for h in range(2):
+            qv = [ex.e4m3[int(c)] for c in q[t, h]]
+            assert got[t, h] == float(0.5 * ex.page_score(page, qv, p % 128 + 1)), (t, h)
+    # rows without a readable local page
+    nan = oracle.oracle_local_scores(q[:2], pool, bt, [0, 1], [-1, 4 * 128 + 5], max_pages=4)
+    assert np.all(np.isnan(nan))
+
+
+def test_local_page_scores_causal_boundary():
+    """A one-hot query reads one dim: of tokens ..., k-1, k, k+1 holding 2, 4
+    and 6 (k = p % 128), the score is 4: the row's own token counts, the next
+    one does not."""
+    for k in (0, 1, 77, 126):
+        page = np.zeros((1, 128, 68), dtype=np.uint8)
+        page[0, :, 64:] = 127                     # scale 1
+        if k > 0:
+            page[0, k - 1, 5] = 0x04              # dim 10 (low nibble of byte 5): 2.0
+        page[0, k, 5] = 0x06                      # 4.0
+        page[0, k + 1, 5] = 0x07                  # 6.0
+        q = np.zeros((1, 1, 128), dtype=np.uint8)
+        q[0, 0, 10] = 0x38                        # 1.0 on dim 10
+        bt = np.array([[0, 0, 0, 0]], dtype=np.int32)
+        got = oracle.oracle_local_scores(q, page.reshape(1, 8704), bt, [0], [3 * 128 + k])
+        assert got[0, 0] == 4.0, (k, got)
+
+
 def test_heap_selection_agrees():
     rng = np.random.default_rng(12)
     for L in [0, 1, 7, 15, 16, 40, 300]:

@@ -36,6 +36,10 @@ PINS = [
     TI.test_nan_token_makes_page_nan_and_ranks_last,
     TI.test_nan_query_element_makes_every_page_nan,
     TI.test_rows_past_max_pages_are_refused,
+    TI.test_local_page_scores_exact_bruteforce,
+    TI.test_local_page_scores_causal_boundary,
+    TFO.test_bruteforce_tiny_rows_local_page_competing,
+    TFO.test_local_page_competes_special_cases,
     TI.test_prefill_row_equals_decode_row_at_same_position,
     TP.test_chunks_against_bruteforce_and_properties,
     TFO.test_bruteforce_tiny_rows,
@@ -158,6 +162,23 @@ _orig_local_pages = I.local_pages
 def _local_pages_clamped(positions, max_pages=None):
     L = _orig_local_pages(positions)
     return L if max_pages is None else np.minimum(L, max_pages)
+
+
+def _local_scores_nt(delta):
+    def f(q, kpage, p):
+        q = np.asarray(q, dtype=np.float64).reshape(-1, 128)
+        nt = int(p) % 128 + 1 + delta
+        return (q @ np.asarray(kpage, dtype=np.float64)[:max(nt, 1)].T).max(axis=1)
+    return f
+
+
+_orig_select_forced = FO.select_forced_row
+
+
+def _forced_local_ignored(scores, L, topk, init_blocks, local_blocks, max_k_tiles,
+                          local_score=None):
+    return _orig_select_forced(scores, L, topk, init_blocks, local_blocks, max_k_tiles,
+                               local_score=-np.inf)
 
 
 def _rows_decode_shifted(seq_lens, query_len):
@@ -284,6 +305,10 @@ MUTATIONS = {
     "sum_not_max": [(I, "page_scores", _page_scores_sum)],
     "page_max_drops_nan": [(I, "page_scores", _page_scores_nanmax)],
     "rows_past_max_pages_clamped": [(I, "local_pages", _local_pages_clamped)],
+    "local_score_misses_own_token": [(I, "local_page_scores", _local_scores_nt(-1))],
+    "local_score_sees_next_token": [(I, "local_page_scores", _local_scores_nt(1))],
+    "local_page_never_wins": [(FO, "select_forced_row", _forced_local_ignored),
+                              (oracle, "select_forced_row", _forced_local_ignored)],
     "decode_positions_shifted": [(I, "rows_decode", _rows_decode_shifted),
                                  (oracle, "rows_decode", _rows_decode_shifted)],
     "prefill_positions_shifted": [(I, "rows_prefill", _rows_prefill_off_by_one),
