@@ -65,6 +65,10 @@ def parse():
                    help="also time the fused qk-norm / rotary / MXFP4 insert of the step's T "
                         "new index-K rows (fp32, RMS norm, rotary dim 64 neox), outside the "
                         "timed step; reported under phases.norm_rope_insert")
+    p.add_argument("--general", metavar="TOPK,INIT,LOCAL",
+                   help="also time the general selection path (score calls writing every "
+                        "history page's score, mi_idx_score_local, mi_idx_select_topk) on the "
+                        "step's rows, outside the timed step; reported under phases.general")
     p.add_argument("--forced", metavar="TOPK,INIT,LOCAL",
                    help="also time the general forced-block selection (mi_idx_select_forced) "
                         "on the step's output, outside the timed step; reported under "
@@ -589,6 +593,59 @@ def main():
             "algorithmic_bytes": sel_bytes,
             "GBps": round(sel_bytes / (sel_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(sel_bytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+    if a.general:
+        topk, init, local = (int(x) for x in a.general.split(","))
+        max_k_tiles = -(-int(np.max(w.seq_lens)) // 128)
+        loc = torch.empty((w.T, w.H), device="cuda")
+        sel = torch.empty((w.T, w.H, topk), dtype=torch.int32, device="cuda")
+        sc_all = torch.empty((w.T, w.H, w.width), device="cuda")
+        pool = dw.pools[0]
+
+        def gen_parts(record):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+            if record:
+                e[0].record(stream)
+            step.plan(dw.sl_dec if w.Rd else None, pre_cu if w.Rp else None,
+                      pre_sl if w.Rp else None, gather_budget_pages=budget)
+            if w.Rd:
+                step.decode(dw.q_dec, pool, dw.bt_dec, dw.sl_dec, dw.out[:dw.nd],
+                            scores_out=sc_all[:dw.nd])
+            if w.Rp:
+                step.prefill(dw.q_pre, pool, dw.bt_pre, dw.cu, dw.sl_pre, dw.ctx, dw.out[dw.nd:],
+                             scores_out=sc_all[dw.nd:])
+            if record:
+                e[1].record(stream)
+            if w.Rd:
+                m.mi_idx_score_local(dw.q_dec, pool, dw.bt_dec, w.width, local_out=loc[:dw.nd],
+                                     seq_lens=dw.sl_dec, query_len=w.query_len)
+            if w.Rp:
+                m.mi_idx_score_local(dw.q_pre, pool, dw.bt_pre, w.width, local_out=loc[dw.nd:],
+                                     cu_seqlens_q=dw.cu, context_lens=dw.ctx)
+            if record:
+                e[2].record(stream)
+            m.mi_idx_select_topk(dw.out, sc_all, topk, init, local, max_k_tiles,
+                                 local_scores=loc, out=sel)
+            if record:
+                e[3].record(stream)
+            return e
+        for _ in range(5):
+            gen_parts(False)
+        evs = [gen_parts(True) for _ in range(10)]
+        torch.cuda.synchronize()
+        med = lambda i, j: float(np.median([x[i].elapsed_time(x[j]) for x in evs]))  # noqa: E731
+        hist_rows = int(alg["pre_flops"] // (w.H * 2 * 128 * 128)) + int(
+            sum(max(0, (int(sl) - w.query_len + i) // 128) for sl in w.dec_seq_lens
+                for i in range(w.query_len)))
+        phases["general"] = {
+            "topk": topk, "init_blocks": init, "local_blocks": local, "max_k_tiles": max_k_tiles,
+            "score_with_all_scores_ms": round(med(0, 1), 4),
+            "local_scores_ms": round(med(1, 2), 4),
+            "select_topk_ms": round(med(2, 3), 4),
+            "rows_x_heads": w.T * w.H,
+            "history_scores": hist_rows * w.H,
+            "select_algorithmic_bytes": hist_rows * w.H * 4 + w.T * w.H * (64 + 4 + 4 * topk),
+            "select_GBps": round((hist_rows * w.H * 4 + w.T * w.H * (64 + 4 + 4 * topk)) /
+                                 (med(2, 3) * 1e-3) / 1e9, 1)}
     if not a.no_ceiling:
         print("[bench] HBM read ceilings", file=sys.stderr, flush=True)
         ceil = hbm_ceilings(torch)

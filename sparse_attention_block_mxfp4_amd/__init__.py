@@ -50,6 +50,9 @@ _SIGS = {
                                          _i64, _i32, _i32, _f32, _vp, _sz, _vp, _vp, _sz, _vp,
                                          _vp, _vp]),
     "mi_idx_select_forced": (_i32, [_vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "mi_idx_score_local": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _i32,
+                                  _i64, _i32, _i32, _f32, _vp, _vp]),
+    "mi_idx_select_topk": (_i32, [_vp, _i64, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp]),
     "mi_idx_norm_rope_insert_mxfp4": (_i32, [_vp, _i32, _i64, _vp, _f32, _vp, _i32, _c.c_double,
                                              _i32, _vp, _i64, _vp, _i64, _vp]),
 }
@@ -349,6 +352,76 @@ def mi_idx_select_forced(ranked, topk, init_blocks, local_blocks, max_k_tiles, o
     st = lib.mi_idx_select_forced(_ptr(ranked), n, int(topk), int(init_blocks),
                                   int(local_blocks), int(max_k_tiles), _ptr(out), _stream(stream))
     _check(st, "mi_idx_select_forced")
+    return out
+
+
+MAX_TOPK = 1024
+
+
+def mi_idx_score_local(q, pages, block_table, max_pages, local_out=None, seq_lens=None,
+                       query_len=None, cu_seqlens_q=None, context_lens=None, scale=1.0,
+                       stream=None):
+    """Causal score of each row's own page ([rows, H] fp32, NaN where a row
+    has none): decode rows from seq_lens and query_len, or prefill rows from
+    cu_seqlens_q and context_lens (device int32 tensors)."""
+    _need(q, "q", _QALL)
+    _need(pages, "pages", _U8)
+    _need(block_table, "block_table", _I32, contiguous=False)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be 2-D with unit column stride")
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [rows, H, 128]")
+    T, H = q.shape[0], q.shape[1]
+    if cu_seqlens_q is None:
+        _need(seq_lens, "seq_lens", _I32)
+        R = seq_lens.numel()
+        ql = int(query_len)
+        if T != R * ql:
+            raise ValueError("decode q must have num_reqs * query_len rows")
+    else:
+        _need(cu_seqlens_q, "cu_seqlens_q", _I32)
+        _need(context_lens, "context_lens", _I32)
+        R = context_lens.numel()
+        ql = 0
+        if cu_seqlens_q.numel() != R + 1:
+            raise ValueError("cu_seqlens_q must have num_reqs + 1 entries")
+    if local_out is None:
+        local_out = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _need(local_out, "local_out", (torch.float32,))
+    if tuple(local_out.shape) != (T, H):
+        raise ValueError(f"local_out must be [{T}, {H}]")
+    st = lib.mi_idx_score_local(_ptr(q), _q_dtype(q), _ptr(pages), pages.numel() // PAGE_BYTES,
+                                _ptr(block_table), block_table.stride(0), _ptr(seq_lens),
+                                _ptr(cu_seqlens_q), _ptr(context_lens), R, ql, T, H,
+                                int(max_pages), float(scale), _ptr(local_out), _stream(stream))
+    _check(st, "mi_idx_score_local")
+    return local_out
+
+
+def mi_idx_select_topk(ranked, scores, topk, init_blocks, local_blocks, max_k_tiles,
+                       local_scores=None, out=None, stream=None):
+    """General selection: ranked [..., 16] and scores [..., W] (a score call's
+    outputs), local_scores [...] (mi_idx_score_local) when the local page can
+    compete; returns out [..., topk] int32."""
+    _need(ranked, "ranked", _I32)
+    _need(scores, "scores", (torch.float32,))
+    if ranked.shape[-1] != TOPK or tuple(scores.shape[:-1]) != tuple(ranked.shape[:-1]):
+        raise ValueError("ranked must be [..., 16] and scores [..., W] over the same rows")
+    n = ranked.numel() // TOPK
+    if local_scores is not None:
+        _need(local_scores, "local_scores", (torch.float32,))
+        if local_scores.numel() != n:
+            raise ValueError("local_scores must hold one score per (row, head)")
+    shape = tuple(ranked.shape[:-1]) + (int(topk),)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=ranked.device)
+    _need(out, "out", _I32)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must be {list(shape)}")
+    st = lib.mi_idx_select_topk(_ptr(scores), scores.shape[-1], _ptr(local_scores), _ptr(ranked),
+                                n, int(topk), int(init_blocks), int(local_blocks),
+                                int(max_k_tiles), _ptr(out), _stream(stream))
+    _check(st, "mi_idx_select_topk")
     return out
 
 

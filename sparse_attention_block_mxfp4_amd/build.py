@@ -11,7 +11,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["api.hip", "insert.hip", "decode.hip", "prefill.hip", "select.hip"]
+SOURCES = ["api.hip", "insert.hip", "decode.hip", "prefill.hip", "select.hip", "general.hip"]
 LIB = os.path.join(HERE, "libmi_idx.so")
 # HBM read-ceiling probes (a measurement aid of the benchmark, not the indexer)
 PROBE_SOURCES = ["probe.hip"]

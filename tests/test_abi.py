@@ -43,7 +43,7 @@ def test_probe_library_exports_its_header(m):
 
 def test_library_exports_every_declared_symbol(m):
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 18
     raw = ctypes.CDLL(m.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -411,3 +411,43 @@ def test_prefill_plan_adversarial_shapes(m):
             assert n == 0 and words[4] == 0
             continue
         _check_plan(words, n, ch, mg, cu, sl, H, budget)
+
+
+def test_general_selection_argument_errors(m):
+    """mi_idx_score_local / mi_idx_select_topk reject bad arguments on the
+    host (nothing launched)."""
+    L = m.lib
+    buf = _fake().ctypes.data
+
+    def local(**kw):
+        a = dict(q=buf, qd=0, pages=buf, nb=10, bt=buf, bts=16, sl=buf, cu=None, ctx=None, R=4,
+                 ql=2, T=8, H=2, mp=16, sc=1.0, out=buf)
+        a.update(kw)
+        return L.mi_idx_score_local(a["q"], a["qd"], a["pages"], a["nb"], a["bt"], a["bts"],
+                                    a["sl"], a["cu"], a["ctx"], a["R"], a["ql"], a["T"], a["H"],
+                                    a["mp"], a["sc"], a["out"], None)
+    assert local(H=9) == m.EUNSUPPORTED
+    assert local(qd=2) == m.EINVAL
+    assert local(sc=0.0) == m.EINVAL
+    assert local(ql=9) == m.EUNSUPPORTED
+    assert local(T=7) == m.EINVAL                      # decode rows = num_reqs * query_len
+    assert local(cu=buf, ctx=None) == m.EINVAL         # prefill rows need context_lens
+    assert local(q=None) == m.EINVAL
+    assert local(nb=0) == m.EINVAL
+    assert local(bts=8) == m.EINVAL
+    assert local(R=0, T=0) == m.OK
+
+    def sel(**kw):
+        a = dict(s=buf, st=16, loc=buf, rk=buf, n=4, topk=8, init=0, local=1, mkt=10, out=buf)
+        a.update(kw)
+        return L.mi_idx_select_topk(a["s"], a["st"], a["loc"], a["rk"], a["n"], a["topk"],
+                                    a["init"], a["local"], a["mkt"], a["out"], None)
+    assert sel(topk=0) == m.EUNSUPPORTED
+    assert sel(topk=m.MAX_TOPK + 1) == m.EUNSUPPORTED
+    assert sel(init=-1) == m.EINVAL
+    assert sel(local=-1) == m.EINVAL
+    assert sel(n=-1) == m.EINVAL
+    assert sel(s=None) == m.EINVAL
+    assert sel(st=0) == m.EINVAL
+    assert sel(local=0, loc=None) == m.EINVAL          # the local page competes
+    assert sel(n=0) == m.OK
