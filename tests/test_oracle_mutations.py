@@ -266,8 +266,10 @@ _orig_windows = FO.forced_windows
 _orig_forced = FO.select_forced_row
 
 
-def _forced_select_ties_high(scores, L, topk, init_blocks, local_blocks, max_k_tiles):
-    s = np.asarray(scores, dtype=np.float64)
+def _forced_select_ties_high(scores, L, topk, init_blocks, local_blocks, max_k_tiles,
+                             local_score=None):
+    s = np.asarray(scores, dtype=np.float64)[:max(L, 0)]
+    s = np.append(s, np.nan if local_score is None else local_score)
     out = np.full(topk, -1, dtype=np.int32)
     if L < 0:
         return out
@@ -283,8 +285,10 @@ def _forced_select_ties_high(scores, L, topk, init_blocks, local_blocks, max_k_t
     return out
 
 
-def _forced_descending(scores, L, topk, init_blocks, local_blocks, max_k_tiles):
-    out = _orig_forced(scores, L, topk, init_blocks, local_blocks, max_k_tiles)
+def _forced_descending(scores, L, topk, init_blocks, local_blocks, max_k_tiles,
+                       local_score=None):
+    out = _orig_forced(scores, L, topk, init_blocks, local_blocks, max_k_tiles,
+                       local_score=local_score)
     ids = out[out >= 0][::-1]
     out[:len(ids)] = ids
     return out
