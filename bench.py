@@ -306,23 +306,26 @@ KERNEL_SOURCES = {"decode_plan_kernel": "decode.hip", "decode_score_kernel": "de
                   "prefill_merge_kernel": "prefill.hip", "insert_kernel": "insert.hip"}
 def profile_commands(workload):
     """The rocprofv3 runs behind profiles/<workload>_kernels.txt (W = the
-    workload option, empty for the default mixed step)."""
+    workload option, empty for the default mixed step).  Counter passes run
+    two steps after one warm-up step (no time-bounded warm-up), without the
+    HBM-ceiling probes."""
     W = "" if workload == "mixed_step" else f" --workload {workload}"
+    short = f"--steps 2 --warmup 1 --warmup-seconds 0 --no-cpu-baseline --no-ceiling{W}"
     return [
         ("kernel trace + stats (the bench's own timed configuration)",
          "rocprofv3 --kernel-trace --stats -T -f csv -d DIR/prof_trace -o trace"
-         f" -- python bench.py --no-cpu-baseline{W}"),
+         f" -- python bench.py --no-cpu-baseline --no-ceiling{W}"),
         ("FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_fetch -o fetch"
-         f" -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline{W}"),
+         f" -- python bench.py {short}"),
         ("WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_write -o write"
-         f" -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline{W}"),
+         f" -- python bench.py {short}"),
         ("copy calibration, FETCH_SIZE", "rocprofv3 --pmc FETCH_SIZE -T -f csv -d DIR/prof_copyf"
          " -o copyf -- python bench.py --copy-calibration"),
         ("copy calibration, WRITE_SIZE", "rocprofv3 --pmc WRITE_SIZE -T -f csv -d DIR/prof_copyw"
          " -o copyw -- python bench.py --copy-calibration"),
         ("SQ counters", "rocprofv3 --pmc SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS "
          "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE -T -f csv "
-         f"-d DIR/prof_sq -o sq -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline{W}"),
+         f"-d DIR/prof_sq -o sq -- python bench.py {short}"),
         ("summary", f"python bench.py --summarize-profiles DIR{W}"),
     ]
 
