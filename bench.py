@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--warmup-seconds", type=float, default=0.25)
     p.add_argument("--no-ceiling", action="store_true",
-                   help="skip the HBM read-ceiling probes (libmi_idx_probe.so)")
+                   help="skip the HBM read and MFMA ceiling probes (libmi_idx_probe.so)")
     p.add_argument("--workload", default="mixed_step")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--pool-copies", type=int, default=None,
@@ -203,6 +203,61 @@ def hbm_ceilings(torch, reps=5):
     out["bytes"] = {"read_stream": int(buf.numel()), "random_pages": int(npages * 8704)}
     del buf, pool, order, sink
     torch.cuda.empty_cache()
+    return out
+
+
+def mfma_ceilings(torch, reps=5, iters=20000):
+    """Matrix-core ceilings of this GPU, for the prefill phase to be reported
+    against next to the dense specification figures: the scaled FP4 x FP8
+    16x16x128 MFMA the scorer issues, and the bf16 16x16x32 MFMA of a
+    bfloat16 query, each as 8 accumulating chains per wave (the instruction's
+    rate) and as the scorer's zeroed-accumulator + max3-fold pipeline, with
+    1 and 2 workgroups of 4 waves per compute unit (1 and 2 waves per SIMD).
+    Median of ``reps`` launches each, HIP events on the launching stream; the
+    shader clock under load is workgroup 0's shader-clock ticks over its
+    wall-clock ticks."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_block_mxfp4_amd",
+                                   "libmi_idx_probe.so"))
+    vp, i64, ci, cu = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+    lib.mi_idx_probe_mfma.argtypes = [ci, ci, ci, ci, cu, cu, vp, i64, vp, vp]
+    cus, clk, wall = ci(), ci(), ci()
+    if lib.mi_idx_probe_device(ctypes.byref(cus), ctypes.byref(clk), ctypes.byref(wall)) != 0:
+        raise RuntimeError("mi_idx_probe_device failed")
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(cus.value * 2 * 256, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    out = {"compute_units": cus.value, "clock_MHz_reported": clk.value / 1e3}
+    flops_per = {"scaled_fp4_fp8_16x16x128": 65536, "bf16_16x16x32": 16384}
+    for kind, name in enumerate(flops_per):
+        for fold, mode in ((0, "chains"), (1, "fold")):
+            for bpc in (1, 2):
+                def call():
+                    st = lib.mi_idx_probe_mfma(kind, fold, iters, bpc, 0x22222222, 0x38383838,
+                                               sink.data_ptr(), sink.numel(),
+                                               clocks.data_ptr(), stream.cuda_stream)
+                    if st != 0:
+                        raise RuntimeError(f"mi_idx_probe_mfma failed with status {st}")
+                call()
+                ts = []
+                for _ in range(reps):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    call()
+                    e1.record(stream)
+                    ts.append((e0, e1))
+                torch.cuda.synchronize()
+                ms = float(np.median([x.elapsed_time(y) for x, y in ts]))
+                flops = cus.value * bpc * 4 * iters * 8 * flops_per[name]
+                out[f"{name}_{mode}_{bpc}_waves_per_simd_TFLOPs"] = round(
+                    flops / (ms * 1e-3) / 1e12, 1)
+                if kind == 0 and fold == 0 and bpc == 2:
+                    shader, wall_ticks = (int(x) for x in clocks.cpu())
+                    out["clock_MHz_under_mfma_load"] = round(
+                        shader / (wall_ticks / (wall.value * 1e3)) / 1e6, 1)
+    out["spec_TFLOPs"] = {"fp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS}
+    del sink, clocks
     return out
 
 
@@ -657,6 +712,13 @@ def main():
             roof_dec["frac_of_read_stream"] = round(dec_gbps / ceil["read_stream_GBps"], 4)
             roof_dec["frac_of_random_pages"] = round(
                 dec_gbps / ceil["random_pages_2_per_wave_GBps"], 4)
+        print("[bench] MFMA ceilings", file=sys.stderr, flush=True)
+        mc = mfma_ceilings(torch)
+        res["mfma_ceiling"] = mc
+        if w.Rp:
+            inst = "bf16_16x16x32" if w.q_dtype == "bf16" else "scaled_fp4_fp8_16x16x128"
+            roof_pre["frac_of_instruction_rate"] = round(
+                pre_tflops / mc[f"{inst}_chains_2_waves_per_simd_TFLOPs"], 4)
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

@@ -30,15 +30,28 @@ def m():
 
 
 def test_probe_library_exports_its_header(m):
-    """libmi_idx_probe.so (the benchmark's HBM read-ceiling probes) exports
-    what include/mi_idx_probe.h declares."""
+    """libmi_idx_probe.so (the benchmark's HBM read and MFMA ceiling probes)
+    exports what include/mi_idx_probe.h declares, and its argument checks
+    refuse before any launch."""
     txt = open(os.path.join(ROOT, "include", "mi_idx_probe.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     names = sorted(set(re.findall(r"\b(mi_idx_probe_[a-z_0-9]+)\s*\(", txt)))
-    assert names == ["mi_idx_probe_read_pages", "mi_idx_probe_read_stream"]
+    assert names == ["mi_idx_probe_device", "mi_idx_probe_mfma", "mi_idx_probe_read_pages",
+                     "mi_idx_probe_read_stream"]
     raw = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_block_mxfp4_amd", "libmi_idx_probe.so"))
     for n in names:
         assert hasattr(raw, n), n
+    ci, cu, vp, i64 = ctypes.c_int, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int64
+    raw.mi_idx_probe_mfma.argtypes = [ci, ci, ci, ci, cu, cu, vp, i64, vp, vp]
+    raw.mi_idx_probe_device.argtypes = [vp, vp, vp]
+    fake = 1 << 20                      # never dereferenced: refused before any call
+    for kind, fold, iters, bpc, sink, clocks in ((2, 0, 1, 1, fake, fake), (0, 2, 1, 1, fake, fake),
+                                                 (0, 0, 0, 1, fake, fake), (0, 0, 1, 9, fake, fake),
+                                                 (0, 0, 1, 1, None, fake), (1, 1, 1, 1, fake, None),
+                                                 (0, 0, 1, 1, fake, fake + 4)):
+        assert raw.mi_idx_probe_mfma(kind, fold, iters, bpc, 0, 0, sink, 1 << 20, clocks,
+                                     None) == 1
+    assert raw.mi_idx_probe_device(None, None, None) == 1
 
 
 def test_library_exports_every_declared_symbol(m):
