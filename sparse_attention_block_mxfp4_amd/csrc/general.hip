@@ -8,39 +8,24 @@
 // It runs after a score call that wrote every history page's score
 // (scores_out).  Two kernels complete it:
 //   local_score_kernel: the score of each row's own page over its causal
-//     prefix (tokens 0 .. p % 128), one workgroup per row, one thread per
-//     token and head group;
-//   select_general_kernel: per (row, head), the topk - force_begin -
-//     force_end best pages strictly between the two windows (the local page
-//     among them when the trailing window is empty), found by an exact radix
-//     select over the selection keys, written in ascending id order between
-//     the forced windows.
+//     prefix (tokens 0 .. p % 128), on the scorers' block-scaled MFMA: a wave
+//     takes 64 (row, head) columns and runs one 8-tile pass per distinct
+//     local page among them, each column keeping only its own page's tokens
+//     up to its position;
+//   select_general_kernel: per (row, head), one wave finds the
+//     topk - force_begin - force_end best pages strictly between the two
+//     windows (the local page among them when the trailing window is empty)
+//     by an exact radix select over the ordered score bits, ties at the
+//     threshold going to the lower ids, and writes them in ascending id order
+//     between the forced windows.
 #include <cmath>
 
 #include "common.h"
 
 namespace mi_idx {
 
-constexpr int kLocalThreads = 2 * kPageTokens;   // 128 tokens x 2 head groups
-constexpr int kSelThreads = 256;
-
-// E2M1 code -> value (sign in bit 3; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t m = c & 7u;
-  // 1.5 * 2^(e-1) style closed form: m = 2e + mantissa bit
-  const float mag = m < 2u ? 0.5f * (float)m : (m & 1u ? 1.5f : 1.0f) * (float)(1u << ((m >> 1) - 1u));
-  return (c & 8u) ? -mag : mag;
-}
-
-// E4M3 "fn" byte -> value (bias 7, no infinities, 0x7F / 0xFF NaN).
-__device__ __forceinline__ float e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float mag;
-  if (e == 15u && m == 7u) mag = __uint_as_float(0x7FC00000u);
-  else if (e == 0u) mag = ldexpf((float)m, -9);
-  else mag = ldexpf((float)(8u + m), (int)e - 10);
-  return (b & 0x80u) ? -mag : mag;
-}
+constexpr int kLocalWaves = 4;
+constexpr int kSelWaves = 4;
 
 // Row t of a score call -> (request, position): decode rows are
 // r * query_len + i at seq_lens[r] - query_len + i; prefill rows (cu_seqlens_q
@@ -63,178 +48,304 @@ __device__ __forceinline__ void row_position(int64_t t, const int32_t *seq_lens,
   }
 }
 
-// One workgroup per row: thread (head group hg, token t) decodes token t of
-// the row's own page once (its 128 values, scale applied per 32-dim block
-// after the block's exact-product sum) and scores it against heads hg, hg +
-// 2, ...; tokens past p % 128 score -inf.
+// Wave w of the grid takes rows t0 = w * (64 / H) .. + 64 / H - 1; column
+// cg * 16 + (lane & 15) of the wave is (row t0 + col / H, head col % H), as
+// the B operand of four 16x16x128 MFMAs per token tile.  A pass over one
+// page P loads each 16-token tile once (the A operand: token tile * 16 +
+// (lane & 15), the 32 dims of lane group lane >> 4 and their E8M0 scale) and
+// folds output row 4 (lane >> 4) + i -- token tile * 16 + 4 (lane >> 4) + i
+// -- into the column's running maximum if the column's local page is P and
+// the token is within its causal prefix.  A column with no readable local
+// page (padding row, page past max_pages, invalid block-table entry) gets
+// NaN, as a page max over a NaN token would.
 template <bool kBf16>
-__global__ __launch_bounds__(kLocalThreads) void local_score_kernel(
+__global__ __launch_bounds__(64 * kLocalWaves) void local_score_kernel(
     const uint8_t *__restrict__ q, const uint8_t *__restrict__ pages, int64_t num_blocks,
     const int32_t *__restrict__ block_table, int64_t bt_stride,
     const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ ctx, int num_reqs, int query_len, int H, int max_pages,
-    float scale, float *__restrict__ out) {
-  __shared__ float s_q[MI_IDX_MAX_HEADS][kDim];
-  __shared__ float s_max[kLocalThreads / 64][MI_IDX_MAX_HEADS];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tok = tid & (kPageTokens - 1), hg = tid >> 7;
-  int r = 0, p = -1;
-  row_position(t, seq_lens, cu, ctx, num_reqs, query_len, r, p);
-  const int L = p >> 7;
-  int64_t phys = -1;
-  if (p >= 0 && L < max_pages) {
-    const int32_t v = block_table[(int64_t)r * bt_stride + L];
-    if (v >= 0 && (int64_t)v < num_blocks) phys = v;
-  }
-  float *dst = out + t * H;
-  if (phys < 0) {   // no readable local page (the same for the whole workgroup)
-    if (tid < H) dst[tid] = __uint_as_float(0x7FC00000u);
-    return;
-  }
-  for (int i = tid; i < H * kDim; i += kLocalThreads) {
-    const int h = i / kDim, d = i - h * kDim;
-    const int64_t at = (t * H + h) * kDim + d;
-    s_q[h][d] = kBf16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t *>(q)[at] << 16)
-                      : e4m3_value(q[at]);
-  }
-  const bool causal = tok <= (p & (kPageTokens - 1));   // tokens 0 .. p % 128
-  float kv[kDim];
-  float f[4];
-  if (causal) {
-    const uint32_t *w = reinterpret_cast<const uint32_t *>(pages + phys * kPageBytes +
-                                                           tok * kTokenBytes);
-    const uint32_t sw = w[16];
+    const int32_t *__restrict__ ctx, int num_reqs, int query_len, int64_t total_rows, int H,
+    int max_pages, float scale, float *__restrict__ out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t16 = lane & 15, g = lane >> 4;
+  const int rpw = 64 / H;
+  const int64_t t0 = ((int64_t)blockIdx.x * kLocalWaves + wave) * rpw;
+  if (t0 >= total_rows) return;   // whole wave; the kernel has no barrier
+  int64_t phys[4];
+  int pmod[4];
+  v8i bq[kBf16 ? 1 : 4];
+  u32x4 bqh[kBf16 ? 4 : 1][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t sb = (sw >> (8 * b)) & 0xFFu;
-      f[b] = sb == 255u ? __uint_as_float(0x7FC00000u) : ldexpf(1.0f, (int)sb - 127);
+  for (int cg = 0; cg < 4; ++cg) {
+    const int col = cg * 16 + t16;
+    const int rl = col / H, h = col - rl * H;
+    const int64_t T = t0 + rl;
+    phys[cg] = -2;   // -2: no column here, -1: a row without a readable page
+    pmod[cg] = 0;
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bqh[cg][k] = u32x4{0u, 0u, 0u, 0u};
+    } else {
+      bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t word = w[i];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) kv[8 * i + k] = e2m1_value((word >> (4 * k)) & 15u);
-    }
-  }
-  __syncthreads();
-#pragma unroll 1
-  for (int h = hg; h < H; h += 2) {
-    float v = -INFINITY;
-    if (causal) {
-      v = 0.f;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        float acc = 0.f;
-#pragma unroll
-        for (int d = 0; d < 32; ++d) acc = fmaf(kv[32 * b + d], s_q[h][32 * b + d], acc);
-        v += acc * f[b];
+    if (rl < rpw && T < total_rows) {
+      int r = 0, p = -1;
+      row_position(T, seq_lens, cu, ctx, num_reqs, query_len, r, p);
+      phys[cg] = -1;
+      if (p >= 0 && (p >> 7) < max_pages) {
+        const int32_t v = block_table[(int64_t)r * bt_stride + (p >> 7)];
+        if (v >= 0 && (int64_t)v < num_blocks) phys[cg] = v;
+      }
+      pmod[cg] = p & (kPageTokens - 1);
+      if constexpr (kBf16) {
+        load_q_bf16(q + (T * H + h) * (2 * kDim), g, bqh[cg]);
+      } else {
+        const uint8_t *qp = q + (T * H + h) * kDim;
+        const u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
+        const u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
+        bq[cg] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     }
-    // max over the group's 128 tokens (NaN-propagating, as the page maxima)
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = nmax(v, __shfl_xor(v, off, 64));
-    if (lane == 0) s_max[wave][h] = v;
   }
-  __syncthreads();
-  if (tid < H) {
-    const int g = tid & 1;   // head h lives in head group h % 2 = waves 2g, 2g + 1
-    dst[tid] = scale * nmax(s_max[2 * g][tid], s_max[2 * g + 1][tid]);
+  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  bool todo[4];
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) todo[cg] = phys[cg] >= 0;
+  for (;;) {
+    // the next page: the first pending one of the lowest lane with any
+    int64_t cand = -1;
+#pragma unroll
+    for (int cg = 3; cg >= 0; --cg)
+      if (todo[cg]) cand = phys[cg];
+    const uint64_t any = __ballot(cand >= 0);
+    if (any == 0) break;
+    const int src = __builtin_ctzll(any);
+    const int64_t P = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(
+                                     (int)((uint64_t)cand >> 32), src) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cand, src));
+    bool use[4];
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      use[cg] = todo[cg] && phys[cg] == P;
+      todo[cg] = todo[cg] && !use[cg];
+    }
+    const uint8_t *pg = pages + P * kPageBytes;
+#pragma unroll
+    for (int tl = 0; tl < 8; ++tl) {
+      const uint8_t *tp = pg + (tl * 16 + t16) * kTokenBytes;
+      const u32x4a4 a4 = *reinterpret_cast<const u32x4a4 *>(tp + 16 * g);
+      const u32x4 a = {a4.x, a4.y, a4.z, a4.w};
+      const uint32_t sc = tp[64 + g];
+      const int tok0 = tl * 16 + 4 * g;
+#pragma unroll
+      for (int cg = 0; cg < 4; ++cg) {
+        v4f c;
+        if constexpr (kBf16) c = mfma_fp4_bf16(a, bqh[cg], sc);
+        else c = mfma_fp4_fp8(a, bq[cg], sc);
+        const int lim = use[cg] ? pmod[cg] : -1;
+        c.x = tok0 <= lim ? c.x : -INFINITY;
+        c.y = tok0 + 1 <= lim ? c.y : -INFINITY;
+        c.z = tok0 + 2 <= lim ? c.z : -INFINITY;
+        c.w = tok0 + 3 <= lim ? c.w : -INFINITY;
+        m[cg] = fold4(m[cg], c);
+      }
+    }
+  }
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {
+    const float v = max_xor32(max_xor16(m[cg]));
+    const int col = cg * 16 + t16;
+    const int rl = col / H, h = col - rl * H;
+    if (g == 0 && phys[cg] != -2)
+      out[(t0 + rl) * H + h] = phys[cg] >= 0 ? scale * v : __uint_as_float(0x7FC00000u);
   }
 }
 
-// Per (row, head): the forced windows and the take best candidates, ascending.
-__global__ __launch_bounds__(kSelThreads) void select_general_kernel(
+// The score's order bits: the high word of the selection key (NaN lowest,
+// -0 as +0), so that comparing them compares the scores.
+__device__ __forceinline__ uint32_t score_order(float s) {
+  return (uint32_t)(make_key(s, 0) >> 32);
+}
+
+// The LDS operations of one wave take effect in program order; this keeps
+// the compiler from moving them across the phases of a radix pass.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Candidate keys of a row, visited in id order as (id = c0 + lane + 64 i):
+// held in registers (up to 64 * NK candidates) ...
+template <int NK>
+struct RegKeys {
+  uint32_t k[NK];
+  int c0, c1, lane;
+  template <class F>
+  __device__ __forceinline__ void each(F &&f) const {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      if (c0 + 64 * i >= c1) break;
+      const int j = c0 + lane + 64 * i;
+      f(k[i], j, j < c1);
+    }
+  }
+};
+
+// ... or read again from the score row at every visit (longer rows).
+struct StreamKeys {
+  const float *srow;
+  float lsc;
+  int L, c0, c1, lane;
+  template <class F>
+  __device__ __forceinline__ void each(F &&f) const {
+    for (int j0 = c0; j0 < c1; j0 += 64) {
+      const int j = j0 + lane;
+      const bool v = j < c1;
+      f(v ? score_order(j < L ? srow[j] : lsc) : 0u, j, v);
+    }
+  }
+};
+
+// The take best candidates of one row (take < the number of candidates),
+// written ascending to dst.  An exact radix select on the order bits: bits
+// above the highest bit where the candidates differ are common; from there
+// 8-bit digits, each pass counting the keys that match the prefix found so
+// far in a 256-bin LDS histogram and keeping the bin that holds the take-th
+// largest, until that bin is taken whole or every bit is fixed.  Then a
+// candidate is taken if its masked bits exceed the prefix, or equal it and
+// it is among the first `rest` such candidates in id order.
+template <class Keys>
+__device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint32_t *h,
+                                           int32_t *dst, int lane) {
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+  keys.each([&](uint32_t k, int, bool v) {
+    if (v) {
+      kmax = max(kmax, k);
+      kmin = min(kmin, k);
+    }
+  });
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+  }
+  const uint32_t diff = kmax ^ kmin;
+  uint32_t prefix = kmax, pmask = 0xFFFFFFFFu, rest = take;
+  if (diff != 0u) {
+    const int hb = 31 - __builtin_clz(diff);
+    pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+    prefix = kmax & pmask;
+    int sh = max(hb - 7, 0);
+    for (;;) {
+      *reinterpret_cast<u32x4 *>(h + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+      wave_lds_sync();
+      keys.each([&](uint32_t k, int, bool v) {
+        if (v && (k & pmask) == prefix) atomicAdd(&h[(k >> sh) & 255u], 1u);
+      });
+      wave_lds_sync();
+      const u32x4 hb4 = *reinterpret_cast<const u32x4 *>(h + 4 * lane);
+      const uint32_t mine = hb4.x + hb4.y + hb4.z + hb4.w;
+      uint32_t above = mine;   // keys in this lane's bins and every higher lane's
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t x = (uint32_t)__shfl_down((int)above, off, 64);
+        above += lane + off < 64 ? x : 0u;
+      }
+      const uint32_t higher = above - mine;
+      const bool here = higher < rest && rest <= above;   // exactly one lane
+      uint32_t bin = 0u, nrest = 0u, inbin = 0u;
+      if (here) {
+        const uint32_t hv[4] = {hb4.x, hb4.y, hb4.z, hb4.w};
+        uint32_t c = higher;
+        bin = 4u * lane;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          if (c + hv[i] >= rest) {
+            bin = 4u * lane + i;
+            inbin = hv[i];
+            break;
+          }
+          c += hv[i];
+        }
+        nrest = rest - c;
+      }
+      const int src = __builtin_ctzll(__ballot(here));
+      bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
+      nrest = (uint32_t)__builtin_amdgcn_readlane((int)nrest, src);
+      inbin = (uint32_t)__builtin_amdgcn_readlane((int)inbin, src);
+      prefix = (prefix & ~(255u << sh)) | (bin << sh);
+      pmask |= 255u << sh;
+      rest = nrest;
+      if (rest == inbin || sh == 0) break;
+      sh = max(sh - 8, 0);
+      wave_lds_sync();
+    }
+  }
+  uint32_t base = 0u, eqseen = 0u;
+  keys.each([&](uint32_t k, int j, bool v) {
+    const uint32_t mk = k & pmask;
+    const bool eq = v && mk == prefix;
+    const uint64_t meq = __ballot(eq);
+    const bool sel = (v && mk > prefix) || (eq && eqseen + lanes_below(meq) < rest);
+    eqseen += (uint32_t)__builtin_popcountll(meq);
+    const uint64_t ms = __ballot(sel);
+    if (sel) dst[base + lanes_below(ms)] = j;
+    base += (uint32_t)__builtin_popcountll(ms);
+  });
+}
+
+// Per (row, head) = one wave: the forced windows and the take best
+// candidates, ascending.  A row whose local page lies past scores_stride
+// (not a scorer's output) is written as padding.
+template <int NK>
+__global__ __launch_bounds__(64 * kSelWaves) void select_general_kernel(
     const float *__restrict__ scores, int64_t stride, const float *__restrict__ local_scores,
-    const int32_t *__restrict__ ranked, int topk, int init_blocks, int local_blocks,
+    const int32_t *__restrict__ ranked, int64_t n, int topk, int init_blocks, int local_blocks,
     int max_k_tiles, int32_t *__restrict__ out) {
-  __shared__ uint32_t s_hist[256];
-  __shared__ uint32_t s_bin, s_rest;
-  __shared__ uint32_t s_cnt[kSelThreads];
-  const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
+  __shared__ __align__(16) uint32_t s_hist[kSelWaves][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kSelWaves + wave;
+  if (row >= n) return;   // whole wave; the kernel has no barrier
   const int L = ranked[row * kTopk + (kTopk - 1)];   // the row's local page, -1: padding
   int32_t *dst = out + row * topk;
-  if (L < 0) {
-    for (int i = tid; i < topk; i += kSelThreads) dst[i] = -1;
+  if (L < 0 || (int64_t)L > stride) {
+    for (int i = lane; i < topk; i += 64) dst[i] = -1;
     return;
   }
   const int nvp = L + 1;
   if (nvp <= topk) {   // every valid page
-    for (int i = tid; i < topk; i += kSelThreads) dst[i] = i < nvp ? i : -1;
+    for (int i = lane; i < topk; i += 64) dst[i] = i < nvp ? i : -1;
     return;
   }
   const int fb = min(min(init_blocks, max_k_tiles), topk);
   const int fe = min(local_blocks, topk - fb);
   const int take = topk - fb - fe;
   const int c0 = fb, c1 = nvp - fe;   // candidates [c0, c1), take of them
-  for (int i = tid; i < fb; i += kSelThreads) dst[i] = i;
-  for (int i = tid; i < fe; i += kSelThreads) dst[fb + take + i] = nvp - fe + i;
+  for (int i = lane; i < fb; i += 64) dst[i] = i;
+  for (int i = lane; i < fe; i += 64) dst[fb + take + i] = nvp - fe + i;
   if (take == 0) return;
   const float *srow = scores + row * stride;
-  auto key_of = [&](int j) -> uint64_t {
-    return make_key(j < L ? srow[j] : local_scores[row], j);
-  };
-  // Radix select of the take-th largest key, a byte at a time from the top.
-  uint64_t prefix = 0, mask = 0;
-  uint32_t k = (uint32_t)take;
-  for (int byte = 7; byte >= 0; --byte) {
-    s_hist[tid] = 0u;
-    __syncthreads();
-    const int sh = 8 * byte;
-    for (int j = c0 + tid; j < c1; j += kSelThreads) {
-      const uint64_t key = key_of(j);
-      if ((key & mask) == prefix) atomicAdd(&s_hist[(uint32_t)(key >> sh) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {   // wave 0: the bin holding the k-th largest key
-      const uint32_t h0 = s_hist[4 * tid], h1 = s_hist[4 * tid + 1], h2 = s_hist[4 * tid + 2],
-                     h3 = s_hist[4 * tid + 3];
-      const uint32_t mine = h0 + h1 + h2 + h3;
-      uint32_t above = mine;   // bins of this lane and every higher lane
+  const float lsc = c1 > L ? local_scores[row] : 0.f;   // the local page is a candidate
+  if (c1 - c0 <= 64 * NK) {
+    RegKeys<NK> keys;
+    keys.c0 = c0;
+    keys.c1 = c1;
+    keys.lane = lane;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t x = __shfl_down(above, off, 64);
-        above += tid + off < 64 ? x : 0u;
-      }
-      const uint32_t higher = above - mine;   // keys in higher lanes' bins
-      if (higher < k && k <= above) {         // exactly one lane
-        uint32_t c = higher;
-        const uint32_t hb[4] = {h0, h1, h2, h3};
-        int bin = 4 * tid + 3;
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          if (c + hb[i] >= k) { bin = 4 * tid + i; break; }
-          c += hb[i];
-        }
-        s_bin = (uint32_t)bin;
-        s_rest = k - c;
-      }
+    for (int i = 0; i < NK; ++i) {
+      const int j = c0 + lane + 64 * i;
+      keys.k[i] = j < c1 ? score_order(j < L ? srow[j] : lsc) : 0u;
     }
-    __syncthreads();
-    prefix |= (uint64_t)s_bin << sh;
-    mask |= (uint64_t)255u << sh;
-    k = s_rest;
-    __syncthreads();
+    select_row(keys, (uint32_t)take, s_hist[wave], dst + fb, lane);
+  } else {
+    const StreamKeys keys{srow, lsc, L, c0, c1, lane};
+    select_row(keys, (uint32_t)take, s_hist[wave], dst + fb, lane);
   }
-  // prefix is now the take-th largest key: exactly take keys are >= it.
-  // Compaction in id order: thread i owns a contiguous run of candidates.
-  const int count = c1 - c0;
-  const int per = (count + kSelThreads - 1) / kSelThreads;
-  const int a = c0 + tid * per, b = min(c1, a + per);
-  uint32_t n = 0;
-  for (int j = a; j < b; ++j) n += key_of(j) >= prefix ? 1u : 0u;
-  s_cnt[tid] = n;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {   // inclusive scan
-    const uint32_t x = tid >= off ? s_cnt[tid - off] : 0u;
-    __syncthreads();
-    s_cnt[tid] += x;
-    __syncthreads();
-  }
-  uint32_t pos = s_cnt[tid] - n;
-  for (int j = a; j < b; ++j)
-    if (key_of(j) >= prefix) dst[fb + pos++] = j;
 }
 
 }  // namespace mi_idx
@@ -274,17 +385,18 @@ extern "C" int mi_idx_score_local(const void *q, int q_dtype, const uint8_t *pag
   if (num_blocks <= 0) return mi_idx_fail(MI_IDX_EINVAL, "score_local: num_blocks <= 0");
   if (bt_stride < max_pages)
     return mi_idx_fail(MI_IDX_EINVAL, "score_local: bt_stride < max_pages");
-  const dim3 grid((unsigned)total_rows), block(kLocalThreads);
+  const int64_t waves = (total_rows + 64 / num_heads - 1) / (64 / num_heads);
+  const dim3 grid((unsigned)((waves + kLocalWaves - 1) / kLocalWaves)), block(64 * kLocalWaves);
   const uint8_t *qb = static_cast<const uint8_t *>(q);
   hipStream_t s = (hipStream_t)stream;
   if (q_dtype == MI_IDX_Q_BF16)
     hipLaunchKernelGGL(local_score_kernel<true>, grid, block, 0, s, qb, pages, num_blocks,
                        block_table, bt_stride, seq_lens, cu_seqlens_q, context_lens, num_reqs,
-                       query_len, num_heads, max_pages, scale, local_out);
+                       query_len, total_rows, num_heads, max_pages, scale, local_out);
   else
     hipLaunchKernelGGL(local_score_kernel<false>, grid, block, 0, s, qb, pages, num_blocks,
                        block_table, bt_stride, seq_lens, cu_seqlens_q, context_lens, num_reqs,
-                       query_len, num_heads, max_pages, scale, local_out);
+                       query_len, total_rows, num_heads, max_pages, scale, local_out);
   return mi_idx_check_launch("score_local");
 }
 
@@ -311,8 +423,18 @@ extern "C" int mi_idx_select_topk(const float *scores, int64_t scores_stride,
   if (scores_stride < 1) return mi_idx_fail(MI_IDX_EINVAL, "select_topk: scores_stride < 1");
   if ((uintptr_t)ranked % 4 || (uintptr_t)out % 4 || (uintptr_t)scores % 4)
     return mi_idx_fail(MI_IDX_EINVAL, "select_topk: misaligned buffer");
-  hipLaunchKernelGGL(select_general_kernel, dim3((unsigned)n), dim3(kSelThreads), 0,
-                     (hipStream_t)stream, scores, scores_stride, local_scores, ranked, topk,
-                     init_blocks, local_blocks, max_k_tiles, out);
+  // Candidates per row <= scores_stride + 1: registers for up to 64 * NK of
+  // them, longer rows re-read their scores at every pass.
+  const dim3 grid((unsigned)((n + kSelWaves - 1) / kSelWaves)), block(64 * kSelWaves);
+  hipStream_t s = (hipStream_t)stream;
+  if (scores_stride + 1 <= 64 * 8)
+    hipLaunchKernelGGL(select_general_kernel<8>, grid, block, 0, s, scores, scores_stride,
+                       local_scores, ranked, n, topk, init_blocks, local_blocks, max_k_tiles, out);
+  else if (scores_stride + 1 <= 64 * 16)
+    hipLaunchKernelGGL(select_general_kernel<16>, grid, block, 0, s, scores, scores_stride,
+                       local_scores, ranked, n, topk, init_blocks, local_blocks, max_k_tiles, out);
+  else
+    hipLaunchKernelGGL(select_general_kernel<32>, grid, block, 0, s, scores, scores_stride,
+                       local_scores, ranked, n, topk, init_blocks, local_blocks, max_k_tiles, out);
   return mi_idx_check_launch("select_topk");
 }

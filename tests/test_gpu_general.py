@@ -147,3 +147,47 @@ def test_general_selection_argument_errors_and_empty():
     empty = torch.empty((0, 1, 16), dtype=torch.int32, device="cuda")
     assert m.mi_idx_select_topk(empty, torch.empty((0, 1, 5), device="cuda"), 8, 0, 1,
                                 10).shape == (0, 1, 8)
+
+
+def _direct_rows(rng, n, stride):
+    """n synthetic (row, head) rows: local pages L (slot 15 of ranked) from
+    -1 (padding) through stride, and float32 scores of four kinds -- normal,
+    three values only (ties everywhere), a fifth NaN, and signed zeros among
+    tiny numbers."""
+    L = rng.integers(0, stride + 1, size=n).astype(np.int32)
+    L[:6] = [-1, 0, 1, 63, 64, stride]
+    s = rng.normal(3.0, 1.0, size=(n, stride))
+    s[1::4] = rng.integers(0, 3, size=s[1::4].shape)
+    nan = rng.random(size=(n, stride)) < 0.2
+    s[2::4] = np.where(nan[2::4], np.nan, s[2::4])
+    s[3::4] = rng.choice(np.array([0.0, -0.0, 1e-30, -1e-30]), size=s[3::4].shape)
+    loc = rng.normal(3.0, 1.0, size=n)
+    loc[1::4] = rng.integers(0, 3, size=loc[1::4].shape)
+    loc[2::8] = np.nan
+    ranked = np.full((n, 16), -1, dtype=np.int32)
+    ranked[:, 15] = L
+    return ranked, s.astype(np.float32), loc.astype(np.float32)
+
+
+@pytest.mark.parametrize("stride", [300, 900, 2100, 5000])
+def test_select_topk_direct_rows(stride):
+    """mi_idx_select_topk alone, on synthetic rows whose candidates span every
+    register size of the selection (up to 512, 1024, 2048) and rows of more
+    than 2048 candidates (read again at every radix pass), with ties, NaN and
+    signed zeros: the same ids as the oracle's select_forced_row, exactly."""
+    print(f"[gpu-test] direct selection stride={stride}", flush=True)
+    m = lib()
+    rng = np.random.default_rng(stride)
+    ranked, s, loc = _direct_rows(rng, 64, stride)
+    dr, ds, dl = (torch.from_numpy(x).cuda() for x in (ranked, s, loc))
+    for topk, init, local, mkt in ((64, 0, 0, 10 ** 6), (1, 0, 0, 10 ** 6), (300, 2, 0, 10 ** 6),
+                                   (1024, 0, 1, 10 ** 6), (17, 3, 2, 5), (700, 0, 0, 40),
+                                   (16, 1, 0, 10 ** 6)):
+        g = m.mi_idx_select_topk(dr, ds, topk, init, local, mkt, local_scores=dl)
+        torch.cuda.synchronize()
+        g = g.cpu().numpy()
+        for i in range(len(ranked)):
+            Li = int(ranked[i, 15])
+            o = oracle.select_forced_row(s[i, :max(Li, 0)].astype(np.float64), Li, topk, init,
+                                         local, mkt, local_score=float(loc[i]))
+            assert np.array_equal(g[i], o), (stride, topk, init, local, mkt, i, Li)
