@@ -48,7 +48,8 @@ __device__ __forceinline__ void row_position(int64_t t, const int32_t *seq_lens,
   }
 }
 
-// Wave w of the grid takes rows t0 = w * (64 / H) .. + 64 / H - 1; column
+// Wave w of the grid takes rows t0 = w * rpw .. + rpw - 1 (rpw = 64 / H
+// prefill rows, or one decode request's query_len rows); column
 // cg * 16 + (lane & 15) of the wave is (row t0 + col / H, head col % H), as
 // the B operand of four 16x16x128 MFMAs per token tile.  A pass over one
 // page P loads each 16-token tile once (the A operand: token tile * 16 +
@@ -67,9 +68,19 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_score_kernel(
     int max_pages, float scale, float *__restrict__ out) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t16 = lane & 15, g = lane >> 4;
-  const int rpw = 64 / H;
+  // rows per wave: 64 // H consecutive prefill rows (one or two local pages),
+  // or the query_len rows of one decode request (their own local pages; a
+  // wave spanning several requests would walk their pages one after another)
+  const int rpw = cu == nullptr ? query_len : 64 / H;
   const int64_t t0 = ((int64_t)blockIdx.x * kLocalWaves + wave) * rpw;
   if (t0 >= total_rows) return;   // whole wave; the kernel has no barrier
+  // the request of the wave's first row (prefill rows), found once
+  int r0 = 0;
+  if (cu != nullptr) {
+    int p0 = 0;
+    row_position(t0, seq_lens, cu, ctx, num_reqs, query_len, r0, p0);
+    r0 = __builtin_amdgcn_readfirstlane(r0);
+  }
   int64_t phys[4];
   int pmod[4];
   v8i bq[kBf16 ? 1 : 4];
@@ -88,8 +99,14 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_score_kernel(
       bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     }
     if (rl < rpw && T < total_rows) {
-      int r = 0, p = -1;
-      row_position(T, seq_lens, cu, ctx, num_reqs, query_len, r, p);
+      int r = r0, p = -1;
+      if (cu == nullptr) {
+        r = (int)(T / query_len);
+        p = seq_lens[r] - query_len + (int)(T - (int64_t)r * query_len);
+      } else {
+        while (r + 1 < num_reqs && cu[r + 1] <= T) ++r;   // rows are consecutive
+        p = ctx[r] + (int)(T - cu[r]);
+      }
       phys[cg] = -1;
       if (p >= 0 && (p >> 7) < max_pages) {
         const int32_t v = block_table[(int64_t)r * bt_stride + (p >> 7)];
@@ -179,8 +196,9 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Candidate keys of a row, visited in id order as (id = c0 + lane + 64 i):
-// held in registers (up to 64 * NK candidates) ...
+// Candidate keys of a row, visited in id order as (id = c0 + lane + 64 i),
+// slots past the last candidate holding key 0: held in registers (up to
+// 64 * NK candidates) ...
 template <int NK>
 struct RegKeys {
   uint32_t k[NK];
@@ -215,19 +233,22 @@ struct StreamKeys {
 // written ascending to dst.  An exact radix select on the order bits: bits
 // above the highest bit where the candidates differ are common; from there
 // 8-bit digits, each pass counting the keys that match the prefix found so
-// far in a 256-bin LDS histogram and keeping the bin that holds the take-th
-// largest, until that bin is taken whole or every bit is fixed.  Then a
-// candidate is taken if its masked bits exceed the prefix, or equal it and
-// it is among the first `rest` such candidates in id order.
+// far in a 256-bin LDS histogram (a key that does not match counts in a junk
+// bin of its lane's, so the pass has no branch) and keeping the bin that
+// holds the take-th largest, until that bin is taken whole or every bit is
+// fixed.  Then a candidate is taken if its masked bits exceed the prefix, or
+// equal it and it is among the first `rest` such candidates in id order.
+// The padding slots (key 0, ids past every candidate) take part in the
+// counts: they tie with the lowest possible key and come last in id order,
+// and take < the candidates, so the take-th largest is a candidate's key, a
+// bin holding padding is never taken whole, and no padding slot is chosen.
 template <class Keys>
 __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint32_t *h,
                                            int32_t *dst, int lane) {
   uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
   keys.each([&](uint32_t k, int, bool v) {
-    if (v) {
-      kmax = max(kmax, k);
-      kmin = min(kmin, k);
-    }
+    kmax = max(kmax, k);
+    kmin = min(kmin, v ? k : 0xFFFFFFFFu);
   });
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -235,7 +256,9 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
   }
   const uint32_t diff = kmax ^ kmin;
-  uint32_t prefix = kmax, pmask = 0xFFFFFFFFu, rest = take;
+  // inbin: keys matching the final prefix; unknown (every candidate equal)
+  // counts as ties
+  uint32_t prefix = kmax, pmask = 0xFFFFFFFFu, rest = take, inbin = 0xFFFFFFFFu;
   if (diff != 0u) {
     const int hb = 31 - __builtin_clz(diff);
     pmask = hb == 31 ? 0u : ~((2u << hb) - 1u);
@@ -243,9 +266,10 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
     int sh = max(hb - 7, 0);
     for (;;) {
       *reinterpret_cast<u32x4 *>(h + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+      h[256 + lane] = 0u;
       wave_lds_sync();
-      keys.each([&](uint32_t k, int, bool v) {
-        if (v && (k & pmask) == prefix) atomicAdd(&h[(k >> sh) & 255u], 1u);
+      keys.each([&](uint32_t k, int, bool) {
+        atomicAdd(&h[(k & pmask) == prefix ? (k >> sh) & 255u : 256u + lane], 1u);
       });
       wave_lds_sync();
       const u32x4 hb4 = *reinterpret_cast<const u32x4 *>(h + 4 * lane);
@@ -258,7 +282,7 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
       }
       const uint32_t higher = above - mine;
       const bool here = higher < rest && rest <= above;   // exactly one lane
-      uint32_t bin = 0u, nrest = 0u, inbin = 0u;
+      uint32_t bin = 0u, nrest = 0u, nin = 0u;
       if (here) {
         const uint32_t hv[4] = {hb4.x, hb4.y, hb4.z, hb4.w};
         uint32_t c = higher;
@@ -267,7 +291,7 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
         for (int i = 3; i >= 0; --i) {
           if (c + hv[i] >= rest) {
             bin = 4u * lane + i;
-            inbin = hv[i];
+            nin = hv[i];
             break;
           }
           c += hv[i];
@@ -276,27 +300,36 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
       }
       const int src = __builtin_ctzll(__ballot(here));
       bin = (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
-      nrest = (uint32_t)__builtin_amdgcn_readlane((int)nrest, src);
-      inbin = (uint32_t)__builtin_amdgcn_readlane((int)inbin, src);
+      rest = (uint32_t)__builtin_amdgcn_readlane((int)nrest, src);
+      inbin = (uint32_t)__builtin_amdgcn_readlane((int)nin, src);
       prefix = (prefix & ~(255u << sh)) | (bin << sh);
       pmask |= 255u << sh;
-      rest = nrest;
       if (rest == inbin || sh == 0) break;
       sh = max(sh - 8, 0);
       wave_lds_sync();
     }
   }
-  uint32_t base = 0u, eqseen = 0u;
-  keys.each([&](uint32_t k, int j, bool v) {
-    const uint32_t mk = k & pmask;
-    const bool eq = v && mk == prefix;
-    const uint64_t meq = __ballot(eq);
-    const bool sel = (v && mk > prefix) || (eq && eqseen + lanes_below(meq) < rest);
-    eqseen += (uint32_t)__builtin_popcountll(meq);
-    const uint64_t ms = __ballot(sel);
-    if (sel) dst[base + lanes_below(ms)] = j;
-    base += (uint32_t)__builtin_popcountll(ms);
-  });
+  uint32_t base = 0u;
+  if (rest == inbin) {   // the threshold bin is taken whole: no tie to break
+    keys.each([&](uint32_t k, int j, bool) {
+      const bool sel = (k & pmask) >= prefix;
+      const uint64_t ms = __ballot(sel);
+      if (sel) dst[base + lanes_below(ms)] = j;
+      base += (uint32_t)__builtin_popcountll(ms);
+    });
+  } else {
+    uint32_t eqseen = 0u;
+    keys.each([&](uint32_t k, int j, bool) {
+      const uint32_t mk = k & pmask;
+      const bool eq = mk == prefix;
+      const uint64_t meq = __ballot(eq);
+      const bool sel = mk > prefix || (eq && eqseen + lanes_below(meq) < rest);
+      eqseen += (uint32_t)__builtin_popcountll(meq);
+      const uint64_t ms = __ballot(sel);
+      if (sel) dst[base + lanes_below(ms)] = j;
+      base += (uint32_t)__builtin_popcountll(ms);
+    });
+  }
 }
 
 // Per (row, head) = one wave: the forced windows and the take best
@@ -307,7 +340,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_general_kernel(
     const float *__restrict__ scores, int64_t stride, const float *__restrict__ local_scores,
     const int32_t *__restrict__ ranked, int64_t n, int topk, int init_blocks, int local_blocks,
     int max_k_tiles, int32_t *__restrict__ out) {
-  __shared__ __align__(16) uint32_t s_hist[kSelWaves][256];
+  __shared__ __align__(16) uint32_t s_hist[kSelWaves][256 + 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * kSelWaves + wave;
   if (row >= n) return;   // whole wave; the kernel has no barrier
@@ -338,6 +371,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_general_kernel(
     keys.lane = lane;
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
+      if (c0 + 64 * i >= c1) break;   // the keys past it are never visited
       const int j = c0 + lane + 64 * i;
       keys.k[i] = j < c1 ? score_order(j < L ? srow[j] : lsc) : 0u;
     }
@@ -385,7 +419,9 @@ extern "C" int mi_idx_score_local(const void *q, int q_dtype, const uint8_t *pag
   if (num_blocks <= 0) return mi_idx_fail(MI_IDX_EINVAL, "score_local: num_blocks <= 0");
   if (bt_stride < max_pages)
     return mi_idx_fail(MI_IDX_EINVAL, "score_local: bt_stride < max_pages");
-  const int64_t waves = (total_rows + 64 / num_heads - 1) / (64 / num_heads);
+  // a decode request's query_len * num_heads <= 64 columns fit one wave
+  const int rpw = prefill ? 64 / num_heads : query_len;
+  const int64_t waves = (total_rows + rpw - 1) / rpw;
   const dim3 grid((unsigned)((waves + kLocalWaves - 1) / kLocalWaves)), block(64 * kLocalWaves);
   const uint8_t *qb = static_cast<const uint8_t *>(q);
   hipStream_t s = (hipStream_t)stream;
