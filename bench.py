@@ -155,6 +155,60 @@ def measured_traffic(kernels, source, workload="mixed_step"):
     return int(sum(found.values()))
 
 
+class TimingEvent:
+    """A HIP timing event created with hipEventDisableSystemFence.  Recording
+    a default event performs a system-scope fence (caches written back and
+    invalidated), which left the GPU idle for about 5 us between the kernels
+    around it and inside every interval it opens; this one only timestamps.
+    Created through the HIP runtime already loaded in the process (the same
+    library path, so the same runtime as torch's streams).  Every loop below
+    creates its events before it starts: creating one while the GPU is busy
+    measured as slow as a device synchronisation."""
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            path = next(line.split()[-1] for line in open("/proc/self/maps")
+                        if "libamdhip64.so" in line)
+            h = ctypes.CDLL(path)
+            vp = ctypes.c_void_p
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [vp, vp]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            h.hipEventDestroy.argtypes = [vp]
+            cls._hip = h
+        return cls._hip
+
+    FLAGS = 0x20000000   # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        st = self._runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), self.FLAGS)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream):
+        st = self._hip.hipEventRecord(self.ev, self._ct.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to ``end`` (both completed)."""
+        ms = self._ct.c_float()
+        st = self._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 def hbm_ceilings(torch, reps=5):
     """Read ceilings of this GPU's HBM, for the decode phase to be reported
     against next to the 8 TB/s figure: a coalesced read of a 2 GiB buffer,
@@ -176,16 +230,14 @@ def hbm_ceilings(torch, reps=5):
     order = torch.from_numpy(np.random.default_rng(0).permutation(npages).astype(np.int32)).cuda()
 
     def timed(call, nbytes):
+        ts = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
         call()
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for e0, e1 in ts:
             e0.record(stream)
             st = call()
             e1.record(stream)
             if st != 0:
                 raise RuntimeError(f"probe failed with status {st}")
-            ts.append((e0, e1))
         torch.cuda.synchronize()
         ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
         return round(nbytes / (ms * 1e-3) / 1e9, 1)
@@ -238,15 +290,12 @@ def mfma_ceilings(torch, reps=5, iters=20000):
                                                clocks.data_ptr(), stream.cuda_stream)
                     if st != 0:
                         raise RuntimeError(f"mi_idx_probe_mfma failed with status {st}")
+                ts = [(TimingEvent(), TimingEvent()) for _ in range(reps)]
                 call()
-                ts = []
-                for _ in range(reps):
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
+                for e0, e1 in ts:
                     e0.record(stream)
                     call()
                     e1.record(stream)
-                    ts.append((e0, e1))
                 torch.cuda.synchronize()
                 ms = float(np.median([x.elapsed_time(y) for x, y in ts]))
                 flops = cus.value * bpc * 4 * iters * 8 * flops_per[name]
@@ -499,11 +548,10 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = []
 
-    def one_step(i, record):
+    def one_step(i, e=None):
         pool = dw.pools[i % len(dw.pools)]
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
+        record = e is not None
         if record:
             e[0].record(stream)
         step.plan(dw.sl_dec if w.Rd else None, pre_cu if w.Rp else None,
@@ -518,13 +566,12 @@ def main():
             step.prefill(dw.q_pre, pool, dw.bt_pre, dw.cu, dw.sl_pre, dw.ctx, dw.out[dw.nd:])
         if record:
             e[3].record(stream)
-            ev.append(e)
 
     tw = time.perf_counter()
     nwarm = 0
     while nwarm < a.warmup or time.perf_counter() - tw < a.warmup_seconds:
         for _ in range(10 if nwarm >= a.warmup else 1):
-            one_step(nwarm, False)
+            one_step(nwarm)
             nwarm += 1
         if nwarm >= a.warmup:
             torch.cuda.synchronize()
@@ -532,11 +579,22 @@ def main():
     warm_s = time.perf_counter() - tw
     print(f"[bench] warmup done ({nwarm} steps, {warm_s:.2f} s); timing {a.steps} steps",
           file=sys.stderr, flush=True)
+    # The timed steps carry no events.  The per-phase kernel times come from
+    # the same steps run again right after, with timing events (TimingEvent:
+    # no system-scope fence) around each phase on the stream the kernels are
+    # launched on.
     t0 = time.perf_counter()
     for i in range(a.steps):
-        one_step(i, True)
+        one_step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ev = [[TimingEvent() for _ in range(4)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(a.steps):
+        one_step(i, ev[i])
+    torch.cuda.synchronize()
+    wall_instrumented = time.perf_counter() - t1
 
     plan_ms = np.mean([e[0].elapsed_time(e[1]) for e in ev])
     dec_ms = np.mean([e[1].elapsed_time(e[2]) for e in ev])
@@ -586,6 +644,7 @@ def main():
         "warmup": a.warmup,
         "warmup_run": {"steps": nwarm, "seconds": round(warm_s, 3)},
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_with_phase_events": round(wall_instrumented * 1e3 / a.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -612,15 +671,13 @@ def main():
         call = lambda: m.mi_idx_norm_rope_insert_mxfp4(  # noqa: E731
             k_new, slot_new, ins_pages, norm_weight=wn, norm_eps=1e-6, positions=pos_new,
             rotary_dim=64, rope_base=10000.0, rope_style=0)
+        times = [(TimingEvent(), TimingEvent()) for _ in range(50)]
         for _ in range(20):
             call()
-        times = []
-        for _ in range(50):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for e0, e1 in times:
             e0.record(stream)
             call()
             e1.record(stream)
-            times.append((e0, e1))
         torch.cuda.synchronize()
         ins_ms = float(np.median([x.elapsed_time(y) for x, y in times]))
         ins_bytes = n_ins * (128 * 4 + 68 + 8 + 8)
@@ -633,15 +690,13 @@ def main():
         topk, init, local = (int(x) for x in a.forced.split(","))
         max_k_tiles = -(-int(np.max(w.seq_lens)) // 128)
         sel_out = torch.empty((w.T, w.H, topk), dtype=torch.int32, device="cuda")
+        times = [(TimingEvent(), TimingEvent()) for _ in range(50)]
         for _ in range(20):
             m.mi_idx_select_forced(dw.out, topk, init, local, max_k_tiles, out=sel_out)
-        times = []
-        for _ in range(50):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for e0, e1 in times:
             e0.record(stream)
             m.mi_idx_select_forced(dw.out, topk, init, local, max_k_tiles, out=sel_out)
             e1.record(stream)
-            times.append((e0, e1))
         torch.cuda.synchronize()
         sel_ms = float(np.median([x.elapsed_time(y) for x, y in times]))
         sel_bytes = w.T * w.H * (16 + topk) * 4
@@ -659,8 +714,8 @@ def main():
         sc_all = torch.empty((w.T, w.H, w.width), device="cuda")
         pool = dw.pools[0]
 
-        def gen_parts(record):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        def gen_parts(e=None):
+            record = e is not None
             if record:
                 e[0].record(stream)
             step.plan(dw.sl_dec if w.Rd else None, pre_cu if w.Rp else None,
@@ -686,9 +741,11 @@ def main():
             if record:
                 e[3].record(stream)
             return e
+        evs = [[TimingEvent() for _ in range(4)] for _ in range(10)]
         for _ in range(5):
-            gen_parts(False)
-        evs = [gen_parts(True) for _ in range(10)]
+            gen_parts()
+        for e in evs:
+            gen_parts(e)
         torch.cuda.synchronize()
         med = lambda i, j: float(np.median([x[i].elapsed_time(x[j]) for x in evs]))  # noqa: E731
         hist_rows = int(alg["pre_flops"] // (w.H * 2 * 128 * 128)) + int(

@@ -14,6 +14,8 @@ Every call goes through the C ABI (``mi_idx_*``); this class only owns the
 buffers.
 """
 
+import collections
+
 import torch
 
 from . import (
@@ -26,6 +28,16 @@ from . import (
     mi_idx_score_topk_decode,
     mi_idx_score_topk_prefill,
 )
+
+
+# Pinned staging buffers of the prefill plan, used in turn, and how often a
+# step records an event after its upload.  An event recorded on the stream
+# leaves the GPU idle for a few microseconds between the kernels around it,
+# so not every step records one: an event covers every upload enqueued before
+# it, and a buffer is rewritten only NSTAGE plans after its last use, by
+# which time an event at or after that use exists (GUARD_EVERY < NSTAGE).
+NSTAGE = 16
+GUARD_EVERY = 8
 
 
 class IndexerStep:
@@ -44,19 +56,16 @@ class IndexerStep:
                 dtype=torch.uint8, device=self.device)
         self.pre_plan = self.pre_ws = None
         self.pre_staging = []
-        self._staging_done = []
-        self._next_staging = 0
+        self._plans = 0                       # prefill plans made so far
+        self._guards = collections.deque()    # (plan number, event after its upload)
         self.pre_launch = None
         if max_prefill_reqs > 0:
             nb = mi_idx_prefill_plan_bytes(max_prefill_reqs, max_prefill_rows, self.H)
             self.pre_plan = torch.empty(nb, dtype=torch.uint8, device=self.device)
             self.pre_ws = torch.empty(mi_idx_prefill_workspace_bytes(), dtype=torch.uint8,
                                       device=self.device)
-            # Two pinned staging buffers used in turn: a buffer is rewritten
-            # only after the copy that last read it has completed.
             self.pre_staging = [torch.empty(nb, dtype=torch.uint8, pin_memory=True)
-                                for _ in range(2)]
-            self._staging_done = [None, None]
+                                for _ in range(NSTAGE)]
 
     def plan(self, decode_seq_lens=None, prefill_cu_seqlens_q_host=None,
              prefill_seq_lens_host=None, gather_budget_pages=0, stream=None):
@@ -66,16 +75,22 @@ class IndexerStep:
                                self.dec_plan, self.dec_ws, stream=stream)
         self.pre_launch = None
         if prefill_cu_seqlens_q_host is not None and len(prefill_seq_lens_host) > 0:
-            k = self._next_staging
-            self._next_staging ^= 1
-            if self._staging_done[k] is not None:
-                self._staging_done[k].synchronize()
+            n = self._plans
+            k = n % NSTAGE
+            if n >= NSTAGE:
+                # the upload that last read buffer k must have completed
+                last = n - NSTAGE
+                while self._guards[0][0] < last:
+                    self._guards.popleft()
+                self._guards[0][1].synchronize()
             self.pre_launch = mi_idx_plan_prefill(
                 prefill_cu_seqlens_q_host, prefill_seq_lens_host, self.H, gather_budget_pages,
                 self.pre_staging[k], self.pre_plan, stream=stream)
-            ev = torch.cuda.Event()
-            ev.record(torch.cuda.current_stream() if stream is None else stream)
-            self._staging_done[k] = ev
+            if n % GUARD_EVERY == 0:
+                ev = torch.cuda.Event()
+                ev.record(torch.cuda.current_stream() if stream is None else stream)
+                self._guards.append((n, ev))
+            self._plans = n + 1
 
     def decode(self, q, pages, block_table, seq_lens, out, scale=1.0, scores_out=None,
                stream=None):

@@ -117,7 +117,7 @@ def split_tiles(step):
     ``step`` split into page ranges, read from the pinned staging copy of the
     plan (header word 6 = split tiles, word 7 = their word offset, 8 words
     each)."""
-    k = step._next_staging ^ 1
+    k = (step._plans - 1) % len(step.pre_staging)
     st = step.pre_staging[k].numpy().view(np.int32)
     n, off = int(st[6]), int(st[7])
     return [tuple(int(x) for x in st[off + 8 * i:off + 8 * i + 3]) for i in range(n)]

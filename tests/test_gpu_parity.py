@@ -141,6 +141,35 @@ def test_prefill_work_lists_repeat_and_upper_bounds():
     checker.compare(a, ref, scores, L)
 
 
+def test_back_to_back_steps_through_the_staging_ring():
+    """Forty steps enqueued back to back with no host synchronisation (the
+    prefill plans cycle through the pinned staging ring and its guard
+    events; budgets alternate, so consecutive plans differ), each into an
+    output buffer of its own: every step gives the first step's result, which
+    matches the oracle."""
+    _banner("back-to-back steps, staging ring")
+    m = lib()
+    from sparse_attention_block_mxfp4_amd.step import IndexerStep
+    w = W.make_workload("mixed_small", 3)
+    dw = DeviceWorkload(w, m.mi_idx_insert_mxfp4)
+    step = IndexerStep(w.H, w.width, max_decode_reqs=w.Rd, query_len=max(w.query_len, 1),
+                       max_prefill_reqs=w.Rp, max_prefill_rows=w.n_prefill_rows)
+    outs = []
+    for i in range(40):
+        step.plan(dw.sl_dec, w.cu_seqlens_q, w.seq_lens[w.Rd:],
+                  gather_budget_pages=(0, 1, 7)[i % 3])
+        o = torch.full_like(dw.out, -7)
+        step.decode(dw.q_dec, dw.pool, dw.bt_dec, dw.sl_dec, o[:dw.nd])
+        step.prefill(dw.q_pre, dw.pool, dw.bt_pre, dw.cu, dw.sl_pre, dw.ctx, o[dw.nd:])
+        outs.append(o)
+    torch.cuda.synchronize()
+    first = outs[0].cpu().numpy()
+    ref, scores, L, _ = run_oracle(w)
+    checker.compare(first, ref, scores, L)
+    for i, o in enumerate(outs[1:], 1):
+        assert np.array_equal(o.cpu().numpy(), first), i
+
+
 def test_decode_replan_in_place():
     """Persistent plan/workspace re-planned with new lengths give the same
     result as a fresh allocation."""
