@@ -134,15 +134,16 @@ struct TopList {
     for (int i = 0; i < kHist; ++i) k[i] = 0ull;
   }
   // Insert x with no branch (x = 0 leaves the list unchanged), so the caller's
-  // basic block stays whole for the scheduler.
+  // basic block stays whole for the scheduler.  Every slot compares with x
+  // at once and then takes its own key, x, or its upper neighbour's key: no
+  // chain of dependent compare-exchanges through the list.
   __device__ __forceinline__ void insert_nb(uint64_t x) {
+    bool c[kHist];
 #pragma unroll
-    for (int i = 0; i < kHist; ++i) {
-      const uint64_t hi = k[i] > x ? k[i] : x;
-      const uint64_t lo = k[i] > x ? x : k[i];
-      k[i] = hi;
-      x = lo;
-    }
+    for (int i = 0; i < kHist; ++i) c[i] = k[i] > x;
+#pragma unroll
+    for (int i = kHist - 1; i >= 1; --i) k[i] = c[i] ? k[i] : (c[i - 1] ? x : k[i - 1]);
+    k[0] = c[0] ? k[0] : x;
   }
   // Insert x (no-op when x does not beat the current 15th key).
   __device__ __forceinline__ void insert(uint64_t x) {

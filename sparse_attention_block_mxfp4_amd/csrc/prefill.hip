@@ -351,12 +351,57 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     const int wave_id = stream * NW + wave;
     // Insert every queued key into its column's list; each wave runs as many
     // insertions as its fullest queue holds.
+    // Drain every queue into its list.  With 6 or more keys queued in some
+    // lane, by sorting networks: the (zero-padded) 16 queued keys sorted
+    // descending (bitonic sort), then max(list[i], queue[15 - i]) -- the best
+    // 16 of both, as a bitonic sequence -- and one bitonic merge: 112
+    // compare-exchanges against 15 per inserted key.  With fewer, one
+    // insertion per key.
     auto drain = [&]() {
+      if (__any(nq >= 6)) {
+        uint64_t q[kQueue];
+#pragma unroll
+        for (int i = 0; i < kQueue; ++i) q[i] = i < nq ? s_queue[i][qslot] : 0ull;
+        auto cas = [](uint64_t &a, uint64_t &b) {   // a >= b afterwards
+          const bool sw = a < b;
+          const uint64_t t = a;
+          a = sw ? b : a;
+          b = sw ? t : b;
+        };
+#pragma unroll
+        for (int k = 2; k <= 16; k <<= 1)
+#pragma unroll
+          for (int j = k >> 1; j >= 1; j >>= 1)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int l = i ^ j;
+              if (l > i) {
+                if ((i & k) == 0) cas(q[i], q[l]);
+                else cas(q[l], q[i]);
+              }
+            }
+        uint64_t c[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint64_t a = i < kHist ? top.k[i] : 0ull, b = q[15 - i];
+          c[i] = a > b ? a : b;
+        }
+#pragma unroll
+        for (int j = 8; j >= 1; j >>= 1)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int l = i ^ j;
+            if (l > i) cas(c[i], c[l]);
+          }
+#pragma unroll
+        for (int i = 0; i < kHist; ++i) top.k[i] = c[i];
+      } else {
 #pragma unroll 1
-      for (int i = 0; i < kQueue; ++i) {
-        if (!__any(i < nq)) break;
-        const uint64_t v = s_queue[i][qslot];
-        top.insert_nb(i < nq ? v : 0ull);
+        for (int i = 0; i < kQueue; ++i) {
+          if (!__any(i < nq)) break;
+          const uint64_t v = s_queue[i][qslot];
+          top.insert_nb(i < nq ? v : 0ull);
+        }
       }
       nq = 0;
     };
