@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_FP8_TFLOPS = 5000.0        # dense FP8 MFMA (the FP8 x FP4 scaled MFMA runs at this rate)
 PEAK_BF16_TFLOPS = 2500.0       # dense bf16 MFMA (the path of a bf16 index-Q)
+PEAK_FP4_TFLOPS = 10100.0       # dense MXFP4 x MXFP4 (both operands FP4; quoted, not the bound)
 METRIC = "index-K GB/s + query-rows/s (decode, prefill), % of HBM/MFMA peak, 1 GPU"
 
 
@@ -634,6 +635,11 @@ def main():
                 "traffic": (measured_traffic(pre_kernels, "prefill.hip", a.workload)
                             if w.q_dtype == "e4m3" else None),
                 "kernel": " + ".join(pre_kernels)}
+    if w.q_dtype == "e4m3":
+        # the sheet's FP4 x FP4 figure, for reference: the E4M3 query operand
+        # makes the instruction run at the FP8 rate, the bound used above
+        roof_pre["mxfp4_sheet_peak"] = PEAK_FP4_TFLOPS
+        roof_pre["frac_of_mxfp4_sheet"] = round(pre_tflops / PEAK_FP4_TFLOPS, 4)
     dominant = roof_pre if (w.Rp and pre_ms >= dec_ms) else roof_dec
     res = {
         "metric": METRIC,
