@@ -171,8 +171,11 @@ class TimingEvent:
     def _runtime(cls):
         if cls._hip is None:
             import ctypes
-            path = next(line.split()[-1] for line in open("/proc/self/maps")
-                        if "libamdhip64.so" in line)
+            path = next((line.split()[-1] for line in open("/proc/self/maps")
+                         if "libamdhip64.so" in line), None)
+            if path is None:
+                raise RuntimeError("TimingEvent: the HIP runtime (libamdhip64.so) is not loaded "
+                                   "in this process; initialise torch.cuda first")
             h = ctypes.CDLL(path)
             vp = ctypes.c_void_p
             h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
