@@ -1,7 +1,7 @@
 """Host logic of bench.py, without a GPU: the one-GPU refusal, the algorithmic
 work it divides by (against an independent count from the oracle's row
-positions), and the comment-insensitive source digest that keys the counter
-traffic."""
+positions), the comment-insensitive source digest that keys the counter
+traffic, and the timing event's refusal without a device."""
 
 import os
 import subprocess
@@ -83,3 +83,11 @@ def test_auto_pool_copies_defeat_the_infinity_cache():
     n = bench.auto_pool_copies(89 * mb)                   # decode batch
     assert n == 7 and (n - 1) * 89 * mb >= 2 * 256 * mb
     assert bench.auto_pool_copies(200 * 1024) == 16       # tiny pools: capped
+
+
+def test_timing_event_needs_a_device():
+    """Without a GPU the fence-free timing event refuses with an error (no
+    HIP runtime in the process, or no device behind it), never a crash."""
+    import pytest
+    with pytest.raises(RuntimeError):
+        bench.TimingEvent()
