@@ -69,9 +69,11 @@ def run_oracle(w, pool=None, scale=1.0, max_pages=None):
     return np.concatenate(outs), scs, np.concatenate(Ls), pool
 
 
-def oracle_request_rows(w, r, rows_in_req, scale=1.0):
+def oracle_request_rows(w, r, rows_in_req, scale=1.0, local=False):
     """Oracle outputs of selected rows of request r, from that request's own
-    pages (encoded by the oracle from the generator's K rows)."""
+    pages (encoded by the oracle from the generator's K rows).  With
+    ``local``, also each row's local-page score ([n, H], over the causal
+    prefix of its own page, NaN for a padding row)."""
     k = w.k_rows(r)
     npages = int(w.n_pages[r])
     pages = w.poisoned_pool()[:npages].copy()
@@ -90,7 +92,14 @@ def oracle_request_rows(w, r, rows_in_req, scale=1.0):
     kp = oracle.decode_pages(pages[:hist])
     out, sc, L = oracle.index_rows(q, pos, kp, scale)
     scores = [sc[i, :, :max(int(L[i]), 0)] for i in range(len(rows_in_req))]
-    return T0 + rows_in_req, out, scores, L
+    if not local:
+        return T0 + rows_in_req, out, scores, L
+    loc = np.full((len(rows_in_req), w.H), np.nan)
+    for i, p in enumerate(pos):
+        if p >= 0:
+            kpage = oracle.decode_pages(pages[int(p) // 128:int(p) // 128 + 1])[0]
+            loc[i] = scale * oracle.local_page_scores(q[i], kpage, int(p))
+    return T0 + rows_in_req, out, scores, L, loc
 
 
 def _one_thread_blas():
@@ -98,7 +107,7 @@ def _one_thread_blas():
     threadpool_limits(1)
 
 
-def oracle_rows_parallel(w, jobs, workers=None):
+def oracle_rows_parallel(w, jobs, workers=None, local=False):
     """oracle_request_rows(w, r, rows) for every (r, rows) in ``jobs``, on CPU
     worker processes (fresh interpreters started by spawn: they import only
     numpy, the oracle and the generators, never touch the GPU and run one
@@ -108,7 +117,8 @@ def oracle_rows_parallel(w, jobs, workers=None):
     ctx = multiprocessing.get_context("spawn")
     with ProcessPoolExecutor(max_workers=workers, mp_context=ctx,
                              initializer=_one_thread_blas) as ex:
-        futs = [ex.submit(oracle_request_rows, w, r, np.asarray(rows)) for r, rows in jobs]
+        futs = [ex.submit(oracle_request_rows, w, r, np.asarray(rows), 1.0, local)
+                for r, rows in jobs]
         return [f.result() for f in futs]
 
 

@@ -12,7 +12,7 @@ import torch
 import oracle
 import workloads as W
 from tests import checker
-from tests.gpu_common import lib, run_gpu, run_oracle
+from tests.gpu_common import lib, oracle_rows_parallel, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -191,3 +191,48 @@ def test_select_topk_direct_rows(stride):
             o = oracle.select_forced_row(s[i, :max(Li, 0)].astype(np.float64), Li, topk, init,
                                          local, mkt, local_score=float(loc[i]))
             assert np.array_equal(g[i], o), (stride, topk, init, local, mkt, i, Li)
+
+
+@pytest.mark.slow
+def test_full_size_general_selection():
+    """The mixed step at full size (16 448 rows, 4 heads, 57 768 + 2 174 history
+    pages) through the general path as the benchmark times it: a score call
+    writing every page score, the local scores, and topk 64 with
+    local_blocks = 0.  Against the oracle on every 4th decode request and a
+    whole row tile of each prefill request: local scores within the
+    tolerance, selections rank by rank."""
+    print("[gpu-test] full-size general selection", flush=True)
+    m = lib()
+    w = W.make_workload("mixed_step", 0)
+    out, sd, sp, dw, _ = run_gpu(w, scores=True)
+    gs = torch.from_numpy(np.concatenate([sd, sp])).cuda()
+    del sd, sp
+    loc = _local_scores(w, dw, w.width)
+    mkt = int(-(-int(np.max(w.seq_lens)) // 128))
+    topk = 64
+    g = m.mi_idx_select_topk(dw.out, gs, topk, 0, 0, mkt, local_scores=loc)
+    torch.cuda.synchronize()
+    g, loc_g = g.cpu().numpy(), loc.cpu().numpy().astype(np.float64)
+    del gs
+    M = 256 // w.H
+    jobs = [(r, np.arange(w.query_len)) for r in range(0, w.Rd, 4)]
+    jobs.append((w.Rd, np.arange(8192 - M, 8192)))
+    jobs.append((w.Rd + 1, np.arange(64 * M, 65 * M)))
+    print(f"[gpu-test] oracle on {sum(len(x) for _, x in jobs)} rows", flush=True)
+    compared = 0
+    for T, _, sc, L, lo in oracle_rows_parallel(w, jobs, local=True):
+        for i, t in enumerate(T):
+            for h in range(w.H):
+                if np.isnan(lo[i, h]):
+                    assert np.isnan(loc_g[t, h])
+                    continue
+                base = np.abs(np.append(sc[i][h], lo[i, h])).max()
+                assert abs(loc_g[t, h] - lo[i, h]) <= checker.REL_TOL * base, (t, h)
+        o = [[oracle.select_forced_row(sc[i][h], int(L[i]), topk, 0, 0, mkt,
+                                       local_score=lo[i, h]) for h in range(w.H)]
+             for i in range(len(T))]
+        full = [[np.append(sc[i][h], lo[i, h]) for h in range(w.H)] for i in range(len(T))]
+        checker.compare_forced(g[T], o, full, L, topk, 0, 0, mkt)
+        compared += len(T)
+    print(f"[gpu-test] full-size general selection: {compared} rows x {w.H} heads match",
+          flush=True)
