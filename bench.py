@@ -9,9 +9,11 @@ buffer.  Inputs are resident in HBM before the timed region.  The steps read
 pool copies in turn (two for the mixed step's 0.5 GB of pages, more for
 smaller pools) so that pages are not served from the 256 MB Infinity Cache.
 
-Prints ONE JSON line.  Kernel times come from HIP events recorded on the
-stream the kernels run on, inside the timed steps.  The CPU baseline is the
-oracle timed on a bounded sample of the same workload on this host.
+Prints ONE JSON line.  The timed steps carry no events (``ms_per_step``,
+``value``); per-phase kernel times come from the same steps run again right
+after, with fence-free HIP timing events recorded on the stream the kernels
+run on.  The CPU baseline is the oracle timed on a bounded sample of the same
+workload on this host.
 """
 
 import argparse
