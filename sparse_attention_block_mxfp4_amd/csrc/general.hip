@@ -192,6 +192,39 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// Wave-wide scans in the lanes themselves (DPP), with no LDS round trip:
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from
+// outside the row read 0), then a row's last lane broadcast into the next
+// row (rows 1 and 3) and lane 31 into rows 2 and 3.  A disabled row keeps 0.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp0(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, true);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// Inclusive prefix sum over lanes 0 .. lane.
+__device__ __forceinline__ uint32_t wave_prefix_sum(uint32_t x) {
+  x += dpp0<kRowShr1>(x);
+  x += dpp0<kRowShr2>(x);
+  x += dpp0<kRowShr4>(x);
+  x += dpp0<kRowShr8>(x);
+  x += dpp0<kRowBcast15, 0xA>(x);
+  x += dpp0<kRowBcast31, 0xC>(x);
+  return x;
+}
+
+// Maximum over the wave (0 is the identity: the values are unsigned).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp0<kRowShr1>(x));
+  x = max(x, dpp0<kRowShr2>(x));
+  x = max(x, dpp0<kRowShr4>(x));
+  x = max(x, dpp0<kRowShr8>(x));
+  x = max(x, dpp0<kRowBcast15, 0xA>(x));
+  x = max(x, dpp0<kRowBcast31, 0xC>(x));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
@@ -250,11 +283,8 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
     kmax = max(kmax, k);
     kmin = min(kmin, v ? k : 0xFFFFFFFFu);
   });
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
-  }
+  kmax = wave_max(kmax);
+  kmin = ~wave_max(~kmin);
   const uint32_t diff = kmax ^ kmin;
   // inbin: keys matching the final prefix; unknown (every candidate equal)
   // counts as ties
@@ -274,12 +304,9 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
       wave_lds_sync();
       const u32x4 hb4 = *reinterpret_cast<const u32x4 *>(h + 4 * lane);
       const uint32_t mine = hb4.x + hb4.y + hb4.z + hb4.w;
-      uint32_t above = mine;   // keys in this lane's bins and every higher lane's
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t x = (uint32_t)__shfl_down((int)above, off, 64);
-        above += lane + off < 64 ? x : 0u;
-      }
+      // keys in this lane's bins and every higher lane's
+      const uint32_t incl = wave_prefix_sum(mine);
+      const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl + mine;
       const uint32_t higher = above - mine;
       const bool here = higher < rest && rest <= above;   // exactly one lane
       uint32_t bin = 0u, nrest = 0u, nin = 0u;
@@ -314,7 +341,8 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
     keys.each([&](uint32_t k, int j, bool) {
       const bool sel = (k & pmask) >= prefix;
       const uint64_t ms = __ballot(sel);
-      if (sel) dst[base + lanes_below(ms)] = j;
+      const uint32_t at = base + lanes_below(ms);
+      if (sel && at < take) dst[at] = j;   // exactly take are chosen; the bound is a safety net
       base += (uint32_t)__builtin_popcountll(ms);
     });
   } else {
@@ -326,7 +354,8 @@ __device__ __forceinline__ void select_row(const Keys &keys, uint32_t take, uint
       const bool sel = mk > prefix || (eq && eqseen + lanes_below(meq) < rest);
       eqseen += (uint32_t)__builtin_popcountll(meq);
       const uint64_t ms = __ballot(sel);
-      if (sel) dst[base + lanes_below(ms)] = j;
+      const uint32_t at = base + lanes_below(ms);
+      if (sel && at < take) dst[at] = j;
       base += (uint32_t)__builtin_popcountll(ms);
     });
   }
@@ -369,11 +398,21 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_general_kernel(
     keys.c0 = c0;
     keys.c1 = c1;
     keys.lane = lane;
+    // Every slot's load first, unconditional at an address clamped into the
+    // row's L history scores (L >= 1 here), so all of them are in flight at
+    // once; then the keys.  (Loads behind the slot tests went out one at a
+    // time, each waited for before the next.)
+    float raw[NK];
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      if (c0 + 64 * i >= c1) break;   // the keys past it are never visited
+      if (c0 + 64 * i >= c1) break;   // the slots past it are never visited
+      raw[i] = srow[min(c0 + lane + 64 * i, L - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      if (c0 + 64 * i >= c1) break;
       const int j = c0 + lane + 64 * i;
-      keys.k[i] = j < c1 ? score_order(j < L ? srow[j] : lsc) : 0u;
+      keys.k[i] = j < c1 ? score_order(j < L ? raw[i] : lsc) : 0u;
     }
     select_row(keys, (uint32_t)take, s_hist[wave], dst + fb, lane);
   } else {
