@@ -81,16 +81,25 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_score_kernel(
     row_position(t0, seq_lens, cu, ctx, num_reqs, query_len, r0, p0);
     r0 = __builtin_amdgcn_readfirstlane(r0);
   }
+  // The four column groups' rows are resolved in phases, each phase's loads
+  // for all four issued together: query operands; the request (rows are
+  // consecutive: r0, or a later request past its first row, which is rare);
+  // the position; the block-table entry.
   int64_t phys[4];
   int pmod[4];
+  int64_t Tc[4];
+  int hc[4];
+  bool live[4];
   v8i bq[kBf16 ? 1 : 4];
   u32x4 bqh[kBf16 ? 4 : 1][4];
 #pragma unroll
   for (int cg = 0; cg < 4; ++cg) {
     const int col = cg * 16 + t16;
-    const int rl = col / H, h = col - rl * H;
-    const int64_t T = t0 + rl;
-    phys[cg] = -2;   // -2: no column here, -1: a row without a readable page
+    const int rl = col / H;
+    hc[cg] = col - rl * H;
+    Tc[cg] = t0 + rl;
+    live[cg] = rl < rpw && Tc[cg] < total_rows;
+    phys[cg] = live[cg] ? -1 : -2;   // -2: no column here, -1: a row without a readable page
     pmod[cg] = 0;
     if constexpr (kBf16) {
 #pragma unroll
@@ -98,31 +107,51 @@ __global__ __launch_bounds__(64 * kLocalWaves) void local_score_kernel(
     } else {
       bq[cg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    if (rl < rpw && T < total_rows) {
-      int r = r0, p = -1;
-      if (cu == nullptr) {
-        r = (int)(T / query_len);
-        p = seq_lens[r] - query_len + (int)(T - (int64_t)r * query_len);
-      } else {
-        while (r + 1 < num_reqs && cu[r + 1] <= T) ++r;   // rows are consecutive
-        p = ctx[r] + (int)(T - cu[r]);
-      }
-      phys[cg] = -1;
-      if (p >= 0 && (p >> 7) < max_pages) {
-        const int32_t v = block_table[(int64_t)r * bt_stride + (p >> 7)];
-        if (v >= 0 && (int64_t)v < num_blocks) phys[cg] = v;
-      }
-      pmod[cg] = p & (kPageTokens - 1);
+    if (live[cg]) {
+      const int64_t T = Tc[cg];
       if constexpr (kBf16) {
-        load_q_bf16(q + (T * H + h) * (2 * kDim), g, bqh[cg]);
+        load_q_bf16(q + (T * H + hc[cg]) * (2 * kDim), g, bqh[cg]);
       } else {
-        const uint8_t *qp = q + (T * H + h) * kDim;
+        const uint8_t *qp = q + (T * H + hc[cg]) * kDim;
         const u32x4 lo = *reinterpret_cast<const u32x4 *>(qp + 16 * g);
         const u32x4 hi = *reinterpret_cast<const u32x4 *>(qp + 64 + 16 * g);
         bq[cg] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     }
+  }
+  int rc[4], pc[4];
+  if (cu == nullptr) {
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) rc[cg] = live[cg] ? (int)(Tc[cg] / query_len) : 0;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+      pc[cg] = live[cg] ? seq_lens[rc[cg]] - query_len +
+                              (int)(Tc[cg] - (int64_t)rc[cg] * query_len)
+                        : -1;
+  } else {
+    const int cu1 = r0 + 1 < num_reqs ? cu[r0 + 1] : 0x7FFFFFFF;
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg) {
+      int r = r0;
+      if (live[cg] && Tc[cg] >= cu1) {
+        r = r0 + 1;
+        while (r + 1 < num_reqs && cu[r + 1] <= Tc[cg]) ++r;
+      }
+      rc[cg] = r;
+    }
+#pragma unroll
+    for (int cg = 0; cg < 4; ++cg)
+      pc[cg] = live[cg] ? ctx[rc[cg]] + (int)(Tc[cg] - cu[rc[cg]]) : -1;
+  }
+#pragma unroll
+  for (int cg = 0; cg < 4; ++cg) {
+    const int p = pc[cg];
+    if (live[cg] && p >= 0 && (p >> 7) < max_pages) {
+      const int32_t v = block_table[(int64_t)rc[cg] * bt_stride + (p >> 7)];
+      if (v >= 0 && (int64_t)v < num_blocks) phys[cg] = v;
+    }
+    pmod[cg] = p & (kPageTokens - 1);
   }
   float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   bool todo[4];
