@@ -612,19 +612,53 @@ __global__ __launch_bounds__(kTileCols) void prefill_merge_kernel(
   const int p = context_lens[r] + row0 + rl;
   const int L = p < seq_lens[r] ? local_page(p, max_pages) : -1;
   if (L < 0 && p >= 0 && p < seq_lens[r]) atomicOr(err, 4u);   // refused row
-  TopList top;
-  top.clear();
-#pragma unroll 1
-  for (int s = s0; s < s0 + ns; ++s) {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(ws_lists + ((size_t)s * kTileCols + c) *
-                                                                  kListKeys);
+  // The pieces' lists (16 keys each, sorted, the last one empty) are loaded
+  // four at a time, all in flight together, and folded in with sorting
+  // networks: max(a[i], b[15 - i]) holds the best 16 of the running list a
+  // and list b as a bitonic sequence, which one bitonic merge sorts.
+  uint64_t a[kListKeys];
 #pragma unroll
-    for (int k2 = 0; k2 < kListKeys / 2; ++k2) {
-      const u32x4 v = src[k2];
-      top.insert(((uint64_t)v.y << 32) | v.x);
-      top.insert(((uint64_t)v.w << 32) | v.z);
+  for (int i = 0; i < kListKeys; ++i) a[i] = 0ull;
+  auto cas = [](uint64_t &x, uint64_t &y) {   // x >= y afterwards
+    const bool sw = x < y;
+    const uint64_t t = x;
+    x = sw ? y : x;
+    y = sw ? t : y;
+  };
+#pragma unroll 1
+  for (int sb = s0; sb < s0 + ns; sb += 4) {
+    u32x4 v[4][kListKeys / 2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sl = min(sb + j, s0 + ns - 1);   // past the last list: re-read it, not merged
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(
+          ws_lists + ((size_t)sl * kTileCols + c) * kListKeys);
+#pragma unroll
+      for (int k2 = 0; k2 < kListKeys / 2; ++k2) v[j][k2] = src[k2];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (sb + j >= s0 + ns) break;
+      uint64_t cmb[kListKeys];
+#pragma unroll
+      for (int i = 0; i < kListKeys; ++i) {
+        const u32x4 w = v[j][(kListKeys - 1 - i) >> 1];
+        const uint64_t b = ((kListKeys - 1 - i) & 1) ? (((uint64_t)w.w << 32) | w.z)
+                                                     : (((uint64_t)w.y << 32) | w.x);
+        cmb[i] = a[i] > b ? a[i] : b;
+      }
+#pragma unroll
+      for (int d = kListKeys / 2; d >= 1; d >>= 1)
+#pragma unroll
+        for (int i = 0; i < kListKeys; ++i)
+          if ((i ^ d) > i) cas(cmb[i], cmb[i ^ d]);
+#pragma unroll
+      for (int i = 0; i < kListKeys; ++i) a[i] = cmb[i];
     }
   }
+  TopList top;
+#pragma unroll
+  for (int i = 0; i < kHist; ++i) top.k[i] = a[i];
   write_row(out + (T * H + h) * kTopk, top, L);
 }
 
