@@ -9,7 +9,8 @@
 // (scores_out).  Two kernels complete it:
 //   local_score_kernel: the score of each row's own page over its causal
 //     prefix (tokens 0 .. p % 128), on the scorers' block-scaled MFMA: a wave
-//     takes 64 (row, head) columns and runs one 8-tile pass per distinct
+//     takes up to 64 (row, head) columns (64 // H consecutive prefill rows,
+//     or one decode request's rows) and runs one 8-tile pass per distinct
 //     local page among them, each column keeping only its own page's tokens
 //     up to its position;
 //   select_general_kernel: per (row, head), one wave finds the
