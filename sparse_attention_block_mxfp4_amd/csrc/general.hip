@@ -284,10 +284,19 @@ struct StreamKeys {
   int L, c0, c1, lane;
   template <class F>
   __device__ __forceinline__ void each(F &&f) const {
-    for (int j0 = c0; j0 < c1; j0 += 64) {
-      const int j = j0 + lane;
-      const bool v = j < c1;
-      f(v ? score_order(j < L ? srow[j] : lsc) : 0u, j, v);
+    // four slots' loads in flight at once, at addresses clamped into the
+    // row's L >= 1 history scores
+    for (int j0 = c0; j0 < c1; j0 += 256) {
+      float raw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) raw[u] = srow[min(j0 + 64 * u + lane, L - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (j0 + 64 * u >= c1) break;
+        const int j = j0 + 64 * u + lane;
+        const bool v = j < c1;
+        f(v ? score_order(j < L ? raw[u] : lsc) : 0u, j, v);
+      }
     }
   }
 };
