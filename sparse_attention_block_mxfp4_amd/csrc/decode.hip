@@ -372,11 +372,11 @@ __device__ __forceinline__ int rank_in(const uint64_t *flat, int n2, uint64_t me
 // because the items cover disjoint pages) into the 16 output slots.
 //
 // Any 15 distinct keys bound the 15th best key of the union from below; the
-// 15th largest of the lists' top-K keys (K = ceil(15 / n), capped at 4, so 1
-// once there are 15 lists or more) is such a bound, and every key of the
-// final top-15 is at or above it.  Only lists whose first key reaches the
-// bound hold such keys, and there are at most 15 of them, so at most 225
-// candidates exist; they are gathered and ranked by counting.  When fewer
+// 15th largest of the lists' top-K keys (K = 4 for up to 16 lists, else 1)
+// is such a bound, and every key of the final top-15 is at or above it.
+// Only lists whose first key reaches the bound hold such keys, and there are
+// at most 15 of them (their first keys are among the 15 largest of the
+// top-K keys), so at most 225 candidates exist; they are gathered and ranked by counting.  When fewer
 // than 15 of the top-K keys are non-empty, every non-empty key is gathered
 // (at most 14 non-empty lists x 15).  Lane x holds lists x, x+64, ...: their
 // first four keys come in with two 16-byte loads, the rest only for a list
@@ -414,7 +414,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
     a[j] = src[0];
     b[j] = src[1];
   }
-  const int K = n >= kHist ? 1 : min(kHead, (kHist + n - 1) / n);
+  // Keys per list behind the bound: all four loaded ones for up to 16 lists
+  // (a tight bound: few candidates, few lists read further), the first for
+  // more (the bound's own ranking would cost more than it saves).
+  const int K = n <= 16 ? kHead : 1;
   const int nK = n * K;
 #pragma unroll
   for (int j = 0; j < kListsPerLane; ++j) {
