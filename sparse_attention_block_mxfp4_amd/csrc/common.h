@@ -38,6 +38,16 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const u32x4 &a, const v8i &b,
                                                           (int)a_scale, 0, 127);
 }
 
+// As mfma_fp4_fp8, the A scale taken from byte kSel of the 32-bit word
+// scales (the MFMA's scale byte select).
+template <int kSel>
+__device__ __forceinline__ v4f mfma_fp4_fp8_sel(const u32x4 &a, const v8i &b, uint32_t scales) {
+  v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, z, 4, 0, kSel, (int)scales, 0,
+                                                          127);
+}
+
 // ---- bfloat16 index-Q ------------------------------------------------------
 // The block-scaled MFMA takes FP8/FP6/FP4 operands only, so a bf16 query runs
 // on the bf16 MFMA: the page's FP4 codes are converted to bf16 (exactly: an

@@ -32,7 +32,6 @@ namespace mi_idx {
 constexpr int kTileCols = 256;          // query columns per row tile
 constexpr int kPreHeaderInts = 16;
 constexpr int kPreErrWord = 9;          // plan header word of the error bits
-constexpr int kChunks = kPageBytes / 16;                    // 544 16-byte chunks
 constexpr int kXcds = 8;                // MI355X accelerator complex dies
 constexpr int kPrefillCgw = 4;          // 16-column groups per wave
 constexpr int kPrefillStreams = 2;      // page streams per workgroup
@@ -60,13 +59,19 @@ inline int rows_per_tile(int H) { return kTileCols / H; }
 // slot count.
 // Workspace: partial lists [slot][256 columns][kListKeys] uint64 keys.
 
-// Token of a page that MFMA row t16 of tile tl reads.  A page's score is a
-// max over its tokens, so any assignment that covers the 128 tokens once is
-// correct; the one chosen spreads a tile's LDS reads (dword 17*token + 4*g)
-// over distinct banks.
-__device__ __forceinline__ int page_token(int tl, int t16) {
-  return 32 * (tl >> 1) + 8 * (t16 >> 2) + 4 * (tl & 1) + (t16 & 3);
-}
+// LDS layout of a staged page (8704 bytes, rearranged from the global token
+// records while staging).  Token tile tl of an MFMA chain is tokens 16 tl ..
+// 16 tl + 15; MFMA lane (r, g) = r + 16 g takes token 16 tl + r, dims 32 g ..
+// 32 g + 31 (16 code bytes) and that block's E8M0 scale.
+//   codes: chunk g of token t at 16-byte slot 4 t + (g ^ lds_swz(t & 15)), so
+//     lane (r, g) reads tile tl with one aligned 16-byte read at 1024 tl +
+//     64 r + 16 (g ^ lds_swz(r)); the swizzle puts the chunks of any 8, and
+//     of any 16, consecutive lanes of a read on distinct banks;
+//   scales: after the 8192 code bytes, byte 8 (r + 16 g) + tl holds the scale
+//     of token 16 tl + r, block g, so one 8-byte read gives a lane the scales
+//     of all eight tiles, which the MFMA takes by byte select.
+__device__ __forceinline__ int lds_swz(int r) { return (r >> 2) ^ (r & 2); }
+constexpr int kLdsScales = kPageTokens * 64;   // 8192
 
 // CGW = 16-column MFMA groups per wave: 16 / CGW waves cover the tile's
 // kTileCols = 256 query columns.  NS page streams of such wave sets share the
@@ -88,15 +93,13 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     int32_t *__restrict__ out, float *__restrict__ scores_out, uint32_t *err) {
   constexpr int NW = 16 / CGW;                       // waves per stream
   constexpr int NT = 64 * NW;                        // threads per stream
-  constexpr int kLoads = (kChunks + NT - 1) / NT;    // 16-byte chunks per thread
   static_assert(NS >= 1 && NS <= 2, "one or two page streams");
   static_assert(NS == 1 || kHist * NT * 8 <= NS * kBufs * kPageBytes,
                 "the stream merge reuses the page buffers");
   // kBufs LDS page buffers per stream (a ring: two pages read per block while
-  // the next two are written), each in the page's global byte layout (token
-  // t at 68*t; +16 bytes: the landing slot of the threads that have no chunk
-  // to write).
-  __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][kBufs][kPageBytes + 16];
+  // the next two are written), each in the staged layout above.
+  static_assert(NT == 256, "staging: two code chunks and two scale bytes per thread");
+  __shared__ __attribute__((aligned(16))) uint8_t s_page[NS][kBufs][kPageBytes];
   // Each stream's current 15th key per column, double-buffered by block
   // parity: block b writes slot b & 1 and reads the partner's slot written in
   // block b-1 (a barrier apart).  Keys are distinct, so a key at or below the
@@ -159,10 +162,19 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         }
       }
     }
-    // One 16x16x128 tile of column group cg.
-    auto tile_mfma = [&](const u32x4 &a, int cg, uint32_t sc) -> v4f {
-      if constexpr (kBf16) return mfma_fp4_bf16(a, bqh[cg], sc);
-      else return mfma_fp4_fp8(a, bq[cg], sc);
+    // This lane's code chunk of token tile 0 in a staged page (tile tl at
+    // +1024 tl).
+    const uint32_t code_off = 64u * (uint32_t)t16 + 16u * (uint32_t)(g ^ lds_swz(t16));
+    // One 16x16x128 E4M3 tile of column group cg, token tile tl (its scale:
+    // byte tl & 3 of sc.x or sc.y).
+    auto tile_mfma_sel = [&](const u32x4 &a, int cg, const uint2 &sc, int tl) -> v4f {
+      const uint32_t w = tl < 4 ? sc.x : sc.y;
+      switch (tl & 3) {
+        case 0: return mfma_fp4_fp8_sel<0>(a, bq[cg], w);
+        case 1: return mfma_fp4_fp8_sel<1>(a, bq[cg], w);
+        case 2: return mfma_fp4_fp8_sel<2>(a, bq[cg], w);
+        default: return mfma_fp4_fp8_sel<3>(a, bq[cg], w);
+      }
     };
     // The column this lane owns after the page-max reduction: with 4 groups
     // per wave each lane group owns one; with 2, lane groups g and g^1 both
@@ -172,12 +184,10 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     const int mycol = (wave * CGW + my_cg) * 16 + t16;
     const int my_rl = mycol / H, my_h = mycol - my_rl * H;
     const int64_t myT = q0 + row0 + my_rl;
-    int myL = -1;
-    bool refused = false;   // a row whose history runs past max_pages
+    int myL = -1;   // -1 also for a row refused because its history runs past max_pages
     if (my_rl < nrows && myT < total_q) {
       const int p = ctx + row0 + my_rl;
       myL = p < sl ? local_page(p, max_pages) : -1;
-      refused = p >= 0 && p < sl && myL < 0;
     }
     // Pages of the tile: every row's history is a prefix of 0..J-1.  This
     // piece walks pages jb..je-1 of them; a column takes page j < myLe.
@@ -200,9 +210,10 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     int nq = 0;
     const int qslot = stream * NT + tid;
 
-    // Page pipeline (per stream; step s is the stream's s-th page).  The
-    // 16-byte chunks of step s are loaded into register slot s & 1 (kLoads
-    // chunks per thread), copied into LDS buffer s & 3 a block later, and read
+    // Page pipeline (per stream; step s is the stream's s-th page).  This
+    // thread's share of step s (two code chunks and a scale word) is loaded
+    // into register slot s & 1, written into LDS buffer s & 3 a block later
+    // (rearranged into the staged layout), and read
     // there by the stream's four waves in the block after that: while a block
     // consumes two pages, the next two sit in registers (then LDS) and the two
     // after them are in flight.  Every load is unconditional (chunk and page
@@ -211,22 +222,29 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // them.
     const int32_t *bt = block_table + (int64_t)r * bt_stride;
     const int jlast = je - 1;
-    static_assert(kLoads >= 1 && kLoads <= 3, "page staging takes 1..3 chunks per thread");
-    // slot 0 (even pages): e0..e2, slot 1 (odd pages): o0..o2
-    uint4 e0, e1, e2, o0, o1, o2;
+    // slot 0 (even pages): e0, e1, es; slot 1 (odd pages): o0, o1, os
+    uint4 e0, e1, o0, o1;
+    uint32_t es, os;
     // Validity of the page of step s (bit s & 63), recorded when the page is
     // issued; a step's page is taken 4 steps after its issue, long before the
     // bit is reused 64 steps later.  Wave-uniform, so it lives in SGPRs.
     uint64_t vmask = 0;
-    // This thread's chunks of a page: byte offsets in global memory (the last
-    // chunk re-read by threads past it) and in an LDS buffer (the landing slot
-    // for those threads); loop-invariant.
-    const uint32_t goff0 = 16u * (uint32_t)min(tid, kChunks - 1);
-    const uint32_t goff1 = 16u * (uint32_t)min(tid + NT, kChunks - 1);
-    const uint32_t goff2 = 16u * (uint32_t)min(tid + 2 * NT, kChunks - 1);
-    const uint32_t loff0 = 16u * (uint32_t)min(tid, kChunks);
-    const uint32_t loff1 = 16u * (uint32_t)min(tid + NT, kChunks);
-    const uint32_t loff2 = 16u * (uint32_t)min(tid + 2 * NT, kChunks);
+    // This thread's share of a page (loop-invariant byte offsets): code chunks
+    // q = tid and tid + 256 (token q >> 2, block q & 3; global 68 (q >> 2) +
+    // 16 (q & 3)), and the scale bytes of blocks gs, gs + 1 of token tid >> 1
+    // (its scale word at global 68 (tid >> 1) + 64).
+    auto code_goff = [](int q) { return 68u * (uint32_t)(q >> 2) + 16u * (uint32_t)(q & 3); };
+    auto code_loff = [](int q) {
+      const int t = q >> 2;
+      return 16u * (uint32_t)(4 * t + ((q & 3) ^ lds_swz(t & 15)));
+    };
+    const uint32_t goff0 = code_goff(tid), goff1 = code_goff(tid + NT);
+    const uint32_t loff0 = code_loff(tid), loff1 = code_loff(tid + NT);
+    const int ts = tid >> 1, gs = 2 * (tid & 1);
+    const uint32_t goffs = 68u * (uint32_t)ts + 64u;
+    const uint32_t loffs = (uint32_t)kLdsScales + 8u * (uint32_t)((ts & 15) + 16 * gs) +
+                           (uint32_t)(ts >> 4);   // block gs; block gs + 1 at +128
+    const uint32_t sshift = 8u * (uint32_t)gs;
     // Block-table entry of a step (clamped like the page index).
     auto bt_entry = [&](int step) { return bt[min(jb + NS * step + stream, jlast)]; };
     // The entries of steps step and step + 1 as one vector load (even lanes the
@@ -238,23 +256,26 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // an issued page id outside the pool (every issued page lies inside the
     // piece's range): skipped, reported in the plan's error word
     bool bad = false;
-    auto pf_issue = [&](int step, int phys, uint4 &R0, uint4 &R1, uint4 &R2) {
+    auto pf_issue = [&](int step, int phys, uint4 &R0, uint4 &R1, uint32_t &RS) {
       const bool valid = phys >= 0 && (int64_t)phys < num_blocks;
       bad |= !valid;
       const uint64_t bit = 1ull << (step & 63);
       vmask = valid ? (vmask | bit) : (vmask & ~bit);
-      // wave-uniform page base + this thread's 32-bit chunk offsets
+      // wave-uniform page base + this thread's 32-bit offsets (the code chunks
+      // are 4-byte aligned in global memory)
       const uint8_t *base = pages + (int64_t)(valid ? phys : 0) * kPageBytes;
-      R0 = *reinterpret_cast<const uint4 *>(base + goff0);
-      if (kLoads > 1) R1 = *reinterpret_cast<const uint4 *>(base + goff1);
-      if (kLoads > 2) R2 = *reinterpret_cast<const uint4 *>(base + goff2);
+      const u32x4a4 c0 = *reinterpret_cast<const u32x4a4 *>(base + goff0);
+      const u32x4a4 c1 = *reinterpret_cast<const u32x4a4 *>(base + goff1);
+      R0 = uint4{c0.x, c0.y, c0.z, c0.w};
+      R1 = uint4{c1.x, c1.y, c1.z, c1.w};
+      RS = *reinterpret_cast<const uint32_t *>(base + goffs);
     };
-    auto pf_commit = [&](int buf, const uint4 &R0, const uint4 &R1, const uint4 &R2) {
-      // No branches: a thread without a chunk writes the landing slot.
+    auto pf_commit = [&](int buf, const uint4 &R0, const uint4 &R1, uint32_t RS) {
       uint8_t *d = s_page[stream][buf];
       *reinterpret_cast<uint4 *>(d + loff0) = R0;
-      if (kLoads > 1) *reinterpret_cast<uint4 *>(d + loff1) = R1;
-      if (kLoads > 2) *reinterpret_cast<uint4 *>(d + loff2) = R2;
+      *reinterpret_cast<uint4 *>(d + loff1) = R1;
+      d[loffs] = (uint8_t)(RS >> sshift);
+      d[loffs + 128u] = (uint8_t)(RS >> (sshift + 8u));
     };
     // Partial page maxima of the page in LDS buffer buf: 8 token tiles x CGW
     // MFMAs, tile tl's MFMAs into one accumulator set while tile tl-1's are
@@ -269,14 +290,16 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
 #pragma unroll
         for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
         v4f cx[CGW], cy[CGW];
+        const uint2 sc = *reinterpret_cast<const uint2 *>(pg + kLdsScales + 8 * lane);
 #pragma unroll
         for (int tl = 0; tl < 8; ++tl) {
-          const uint8_t *tp = pg + page_token(tl, t16) * kTokenBytes;
-          const uint32_t *a32 = reinterpret_cast<const uint32_t *>(tp + 16 * g);
-          const float sf = e8m0_scale(tp[64 + g]);
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(pg + code_off + 1024 * tl);
+          const float sf = e8m0_scale(((tl < 4 ? sc.x : sc.y) >> (8 * (tl & 3))) & 0xFFu);
           bf16x8 av[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) av[k] = fp4x8_to_bf16(a32[k], sf);
+          av[0] = fp4x8_to_bf16(a.x, sf);
+          av[1] = fp4x8_to_bf16(a.y, sf);
+          av[2] = fp4x8_to_bf16(a.z, sf);
+          av[3] = fp4x8_to_bf16(a.w, sf);
 #pragma unroll
           for (int cg = 0; cg < CGW; ++cg) {
             v4f c = {0.f, 0.f, 0.f, 0.f};
@@ -297,29 +320,26 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         for (int cg = 0; cg < CGW; ++cg) m[cg] = fold4(m[cg], cy[cg]);
         return;
       }
+      // the scales first: the chain's first MFMA then waits for two reads, not nine
+      const uint2 sc = *reinterpret_cast<const uint2 *>(pg + kLdsScales + 8 * lane);
       u32x4 A[8];
-      uint32_t S[8];
 #pragma unroll
-      for (int tl = 0; tl < 8; ++tl) {
-        const uint8_t *tp = pg + page_token(tl, t16) * kTokenBytes;
-        const u32x4a4 a4 = *reinterpret_cast<const u32x4a4 *>(tp + 16 * g);
-        A[tl] = u32x4{a4.x, a4.y, a4.z, a4.w};
-        S[tl] = tp[64 + g];
-      }
+      for (int tl = 0; tl < 8; ++tl)
+        A[tl] = *reinterpret_cast<const u32x4 *>(pg + code_off + 1024 * tl);
 #pragma unroll
       for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
       v4f cx[CGW], cy[CGW];
 #pragma unroll
-      for (int cg = 0; cg < CGW; ++cg) cx[cg] = tile_mfma(A[0], cg, S[0]);
+      for (int cg = 0; cg < CGW; ++cg) cx[cg] = tile_mfma_sel(A[0], cg, sc, 0);
 #pragma unroll
       for (int tl = 1; tl < 8; ++tl) {
 #pragma unroll
         for (int cg = 0; cg < CGW; ++cg) {
           if (tl & 1) {
-            cy[cg] = tile_mfma(A[tl], cg, S[tl]);
+            cy[cg] = tile_mfma_sel(A[tl], cg, sc, tl);
             m[cg] = fold4(m[cg], cx[cg]);
           } else {
-            cx[cg] = tile_mfma(A[tl], cg, S[tl]);
+            cx[cg] = tile_mfma_sel(A[tl], cg, sc, tl);
             m[cg] = fold4(m[cg], cy[cg]);
           }
         }
@@ -459,16 +479,16 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         s_floor[1][stream][tid] = 0ull;
       }
       if (threadIdx.x < 16) (&s_need[0][0])[threadIdx.x] = 0;
-      pf_issue(0, bt_entry(0), e0, e1, e2);
+      pf_issue(0, bt_entry(0), e0, e1, es);
       __builtin_amdgcn_sched_barrier(0);
-      pf_issue(1, bt_entry(1), o0, o1, o2);
+      pf_issue(1, bt_entry(1), o0, o1, os);
       __builtin_amdgcn_sched_barrier(0);
-      pf_commit(0, e0, e1, e2);
-      pf_commit(1, o0, o1, o2);
+      pf_commit(0, e0, e1, es);
+      pf_commit(1, o0, o1, os);
       __builtin_amdgcn_sched_barrier(0);
-      pf_issue(2, bt_entry(2), e0, e1, e2);
+      pf_issue(2, bt_entry(2), e0, e1, es);
       __builtin_amdgcn_sched_barrier(0);
-      pf_issue(3, bt_entry(3), o0, o1, o2);
+      pf_issue(3, bt_entry(3), o0, o1, os);
       __builtin_amdgcn_sched_barrier(0);
       int bt_a = bt_fetch(4), bt_b = 0;
       lds_barrier();
@@ -486,11 +506,11 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       auto block = [&](int k, int rb, int parity, int bt_use, int &bt_next) {
         auto stage = [&]() {
           __builtin_amdgcn_s_setprio(1);
-          pf_commit(rb ^ 2, e0, e1, e2);
-          pf_commit((rb ^ 2) + 1, o0, o1, o2);
+          pf_commit(rb ^ 2, e0, e1, es);
+          pf_commit((rb ^ 2) + 1, o0, o1, os);
           bt_next = bt_fetch(k + 6);
-          pf_issue(k + 4, __builtin_amdgcn_readlane(bt_use, 0), e0, e1, e2);
-          pf_issue(k + 5, __builtin_amdgcn_readlane(bt_use, 1), o0, o1, o2);
+          pf_issue(k + 4, __builtin_amdgcn_readlane(bt_use, 0), e0, e1, es);
+          pf_issue(k + 5, __builtin_amdgcn_readlane(bt_use, 1), o0, o1, os);
           __builtin_amdgcn_s_setprio(0);
         };
         // A wave issuing its MFMA chain, or staging the next pages, runs at
@@ -553,12 +573,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         for (int i = 0; i < kHist; ++i) top.insert_nb(s_lists[i * NT + tid]);
       }
     }
-    if (kOne) {
-      if (stream == 0 && writer && my_rl < nrows && myT < total_q) {
-        write_row(out + (myT * H + my_h) * kTopk, top, myL);
-        if (refused) atomicOr(err, 4u);
-      }
-    } else if (stream == 0 && writer) {
+    if (stream == 0 && writer) {
       // The piece record and the column's row are read again here rather than
       // kept in registers across the page walk (the asm hides the earlier read).
       const int4 *pv = pieces;
@@ -568,21 +583,22 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       const int rl = mycol / H, h = mycol - rl * H;
       const int64_t T = (int64_t)cu_seqlens_q[fr] + frow0 + rl;
       if (rl < f0.z && T < total_q) {
-      if (fslot < 0) {
-        const int p = context_lens[fr] + frow0 + rl;
-        const int L = p < seq_lens[fr] ? local_page(p, max_pages) : -1;
-        write_row(out + (T * H + h) * kTopk, top, L);
-        if (L < 0 && p >= 0 && p < seq_lens[fr]) atomicOr(err, 4u);   // refused row
-      } else if (ws_lists != nullptr && fslot < kMaxSlots) {
-        u32x4 *dst = reinterpret_cast<u32x4 *>(ws_lists + ((size_t)fslot * kTileCols + mycol) *
-                                                            kListKeys);
+        if (kOne || fslot < 0) {
+          const int p = context_lens[fr] + frow0 + rl;
+          const int L = p < seq_lens[fr] ? local_page(p, max_pages) : -1;
+          write_row(out + (T * H + h) * kTopk, top, L);
+          if (L < 0 && p >= 0 && p < seq_lens[fr]) atomicOr(err, 4u);   // refused row
+        } else if (ws_lists != nullptr && fslot < kMaxSlots) {
+          u32x4 *dst = reinterpret_cast<u32x4 *>(
+              ws_lists + ((size_t)fslot * kTileCols + mycol) * kListKeys);
 #pragma unroll
-        for (int k2 = 0; k2 < kListKeys / 2; ++k2) {
-          const uint64_t x0 = top.k[2 * k2];
-          const uint64_t x1 = 2 * k2 + 1 < kHist ? top.k[2 * k2 + 1] : 0ull;
-          dst[k2] = u32x4{(uint32_t)x0, (uint32_t)(x0 >> 32), (uint32_t)x1, (uint32_t)(x1 >> 32)};
+          for (int k2 = 0; k2 < kListKeys / 2; ++k2) {
+            const uint64_t x0 = top.k[2 * k2];
+            const uint64_t x1 = 2 * k2 + 1 < kHist ? top.k[2 * k2 + 1] : 0ull;
+            dst[k2] = u32x4{(uint32_t)x0, (uint32_t)(x0 >> 32), (uint32_t)x1,
+                            (uint32_t)(x1 >> 32)};
+          }
         }
-      }
       }
     }
     // The next piece's staging rewrites the page buffers read just above.
