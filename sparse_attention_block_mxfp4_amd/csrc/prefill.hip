@@ -125,14 +125,38 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
   const int tid = (int)threadIdx.x - stream * NT;    // thread within its stream
   const int wave = tid >> 6, lane = tid & 63;
   const int t16 = lane & 15, g = lane >> 4;
+  const int pend = kOne ? wl.x + 1 : wl.x + wl.y;
+  // The next piece's record, read ahead while this piece walks its pages:
+  // lane i < 6 of vrec holds word i (request, first row, row count, first
+  // page, end page, slot).  A vector load: the page walk's LDS waits do not
+  // wait for it, as they would for a scalar load.
+  int vrec = 0;
 #pragma unroll 1
-  for (int pi = wl.x; pi < (kOne ? wl.x + 1 : wl.x + wl.y); ++pi) {
-    const int4 pc0 = pieces[2 * pi], pc1 = pieces[2 * pi + 1];
-    const int r = pc0.x, row0 = pc0.y, nrows = pc0.z;
+  for (int pi = wl.x; pi < pend; ++pi) {
+    int r, row0, nrows, pw, px, slot;
+    if (kOne || pi == wl.x) {
+      const int4 pc0 = pieces[2 * pi], pc1 = pieces[2 * pi + 1];
+      r = pc0.x, row0 = pc0.y, nrows = pc0.z, pw = pc0.w, px = pc1.x, slot = pc1.y;
+    } else {
+      r = __builtin_amdgcn_readlane(vrec, 0), row0 = __builtin_amdgcn_readlane(vrec, 1);
+      nrows = __builtin_amdgcn_readlane(vrec, 2), pw = __builtin_amdgcn_readlane(vrec, 3);
+      px = __builtin_amdgcn_readlane(vrec, 4), slot = __builtin_amdgcn_readlane(vrec, 5);
+    }
+    if (!kOne) {
+      const int32_t *nrec = reinterpret_cast<const int32_t *>(pieces) + 8 * (pi + 1);
+      vrec = (pi + 1 < pend && lane < 6) ? nrec[lane] : 0;
+    }
     if (r < 0 || r >= num_reqs) continue;   // the same for every thread
     const int ctx = context_lens[r];
     const int sl = seq_lens[r];
     const int64_t q0 = cu_seqlens_q[r];
+    // What the end of the piece needs, kept in one register through the page
+    // walk (lane i: request, first row, row count, slot, context length,
+    // sequence length, first query row); the empty asm keeps the compiler
+    // from holding the scalar originals instead.
+    int vcur = lane == 0 ? r : lane == 1 ? row0 : lane == 2 ? nrows : lane == 3 ? slot
+             : lane == 4 ? ctx : lane == 5 ? sl : (int)q0;
+    asm volatile("" : "+v"(vcur));
 
     // B operands: columns (wave*CGW + cg)*16 + t16.
     v8i bq[kBf16 ? 1 : CGW];
@@ -197,8 +221,8 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       J = plast >= 0 ? min(plast >> 7, max_pages) : 0;
       J = max(J, 0);
     }
-    const int jb = kOne ? 0 : max(pc0.w, 0);
-    const int je = kOne ? J : max(min(pc1.x, J), jb);
+    const int jb = kOne ? 0 : max(pw, 0);
+    const int je = kOne ? J : max(min(px, J), jb);
     const int myLe = kOne ? myL : min(myL, je);
     // The column's top-15 (registers) and its queue (LDS): a key that beats
     // the list's 15th key (and the partner stream's) is appended to the queue
@@ -561,7 +585,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     if constexpr (NS == 2) {
       // Stream 1 hands its lists to stream 0 through the (now idle) page
       // buffers: key i of thread t at [i * NT + t].  The streams saw disjoint
-      // pages, so inserting one list into the other gives the top-15 of both.
+      // pages, so the best 15 of both lists are the tile's top-15.
       uint64_t *s_lists = reinterpret_cast<uint64_t *>(&s_page[0][0][0]);
       if (stream == 1) {
 #pragma unroll
@@ -569,25 +593,47 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
       }
       lds_barrier();
       if (stream == 0) {
+        // max(a[i], b[15 - i]) of the two sorted lists (each padded with an
+        // empty 16th key) holds the best 16 of both as a bitonic sequence,
+        // which one bitonic merge sorts.
+        uint64_t c[16];
 #pragma unroll
-        for (int i = 0; i < kHist; ++i) top.insert_nb(s_lists[i * NT + tid]);
+        for (int i = 0; i < 16; ++i) {
+          const uint64_t a = i < kHist ? top.k[i] : 0ull;
+          const uint64_t b = i >= 1 ? s_lists[(15 - i) * NT + tid] : 0ull;
+          c[i] = a > b ? a : b;
+        }
+#pragma unroll
+        for (int j = 8; j >= 1; j >>= 1)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int l = i ^ j;
+            if (l > i) {
+              const bool sw = c[i] < c[l];
+              const uint64_t t = c[i];
+              c[i] = sw ? c[l] : c[i];
+              c[l] = sw ? t : c[l];
+            }
+          }
+#pragma unroll
+        for (int i = 0; i < kHist; ++i) top.k[i] = c[i];
       }
     }
     if (stream == 0 && writer) {
-      // The piece record and the column's row are read again here rather than
-      // kept in registers across the page walk (the asm hides the earlier read).
-      const int4 *pv = pieces;
-      asm volatile("" : "+s"(pv));
-      const int4 f0 = pv[2 * pi], f1 = pv[2 * pi + 1];
-      const int fr = f0.x, frow0 = f0.y, fslot = f1.y;
+      const int frow0 = __builtin_amdgcn_readlane(vcur, 1);
+      const int fnrows = __builtin_amdgcn_readlane(vcur, 2);
+      const int fslot = __builtin_amdgcn_readlane(vcur, 3);
+      const int fctx = __builtin_amdgcn_readlane(vcur, 4);
+      const int fsl = __builtin_amdgcn_readlane(vcur, 5);
+      const int fq0 = __builtin_amdgcn_readlane(vcur, 6);
       const int rl = mycol / H, h = mycol - rl * H;
-      const int64_t T = (int64_t)cu_seqlens_q[fr] + frow0 + rl;
-      if (rl < f0.z && T < total_q) {
+      const int64_t T = (int64_t)fq0 + frow0 + rl;
+      if (rl < fnrows && T < total_q) {
         if (kOne || fslot < 0) {
-          const int p = context_lens[fr] + frow0 + rl;
-          const int L = p < seq_lens[fr] ? local_page(p, max_pages) : -1;
+          const int p = fctx + frow0 + rl;
+          const int L = p < fsl ? local_page(p, max_pages) : -1;
           write_row(out + (T * H + h) * kTopk, top, L);
-          if (L < 0 && p >= 0 && p < seq_lens[fr]) atomicOr(err, 4u);   // refused row
+          if (L < 0 && p >= 0 && p < fsl) atomicOr(err, 4u);   // refused row
         } else if (ws_lists != nullptr && fslot < kMaxSlots) {
           u32x4 *dst = reinterpret_cast<u32x4 *>(
               ws_lists + ((size_t)fslot * kTileCols + mycol) * kListKeys);
