@@ -304,7 +304,9 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // Partial page maxima of the page in LDS buffer buf: 8 token tiles x CGW
     // MFMAs, tile tl's MFMAs into one accumulator set while tile tl-1's are
     // folded into m[cg] (this lane's 4 tokens of every tile).  No branches.
-    auto page_fold = [&](int buf, float (&m)[CGW]) {
+    // (pre: the scale word and tile 0's operand, psc and pa0, were read ahead)
+    auto page_fold = [&](int buf, float (&m)[CGW], bool pre = false, uint2 psc = uint2{0u, 0u},
+                         u32x4 pa0 = u32x4{0u, 0u, 0u, 0u}) {
       const uint8_t *pg = s_page[stream][buf];
       if constexpr (kBf16) {
         // bf16 query: each tile's codes are read and converted once (four
@@ -345,10 +347,11 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         return;
       }
       // the scales first: the chain's first MFMA then waits for two reads, not nine
-      const uint2 sc = *reinterpret_cast<const uint2 *>(pg + kLdsScales + 8 * lane);
+      const uint2 sc = pre ? psc : *reinterpret_cast<const uint2 *>(pg + kLdsScales + 8 * lane);
       u32x4 A[8];
+      A[0] = pre ? pa0 : *reinterpret_cast<const u32x4 *>(pg + code_off);
 #pragma unroll
-      for (int tl = 0; tl < 8; ++tl)
+      for (int tl = 1; tl < 8; ++tl)
         A[tl] = *reinterpret_cast<const u32x4 *>(pg + code_off + 1024 * tl);
 #pragma unroll
       for (int cg = 0; cg < CGW; ++cg) m[cg] = -INFINITY;
@@ -541,10 +544,17 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         // raised priority, so that the SIMD's other wave (in its selection
         // step) does not delay the next MFMA or load (about 1.7 % faster on
         // the mixed step in A/B).
+        // Stream 0 opens with its first page's chain: that page's scale word
+        // and first operand tile are read together with the drain flags, so
+        // the chain does not wait for a second LDS round trip after the check
+        // (stream 1 reads them too, unused: cheaper than a branch here).
+        const uint8_t *pg0 = s_page[stream][rb];
+        const uint2 sc0 = *reinterpret_cast<const uint2 *>(pg0 + kLdsScales + 8 * lane);
+        const u32x4 a00 = *reinterpret_cast<const u32x4 *>(pg0 + code_off);
         maybe_drain(parity);
         if (stream == 0) {
           __builtin_amdgcn_s_setprio(1);
-          page_fold(rb, ma);
+          page_fold(rb, ma, true, sc0, a00);
           __builtin_amdgcn_s_setprio(0);
           pin(ma);
           take(page_reduce(mb), k - 1, parity);
