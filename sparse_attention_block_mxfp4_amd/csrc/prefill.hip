@@ -544,10 +544,11 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         // raised priority, so that the SIMD's other wave (in its selection
         // step) does not delay the next MFMA or load (about 1.7 % faster on
         // the mixed step in A/B).
-        // Stream 0 opens with its first page's chain: that page's scale word
-        // and first operand tile are read together with the drain flags, so
-        // the chain does not wait for a second LDS round trip after the check
-        // (stream 1 reads them too, unused: cheaper than a branch here).
+        // The block's first page's scale word and first operand tile are read
+        // together with the drain flags: stream 0's chain on that page then
+        // does not wait for a second LDS round trip after the check, and
+        // stream 1's starts after its selection step and staging with them in
+        // registers.
         const uint8_t *pg0 = s_page[stream][rb];
         const uint2 sc0 = *reinterpret_cast<const uint2 *>(pg0 + kLdsScales + 8 * lane);
         const u32x4 a00 = *reinterpret_cast<const u32x4 *>(pg0 + code_off);
@@ -569,7 +570,7 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
           pin(mb);
           stage();
           __builtin_amdgcn_s_setprio(1);
-          page_fold(rb, ma);
+          page_fold(rb, ma, true, sc0, a00);
           __builtin_amdgcn_s_setprio(0);
           pin(ma);
           take(page_reduce(ma), k, parity);
