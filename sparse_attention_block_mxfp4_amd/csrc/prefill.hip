@@ -464,14 +464,17 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
     // Offer page j's max to the column's list (step < 0, past the row's
     // history or the piece, or an invalid page: nothing).  Branch-free: the
     // queue write always happens, the count moves only for a key above the
-    // filter bound.
-    auto take = [&](float v, int step, int parity) {
+    // filter bound.  Both selection steps of a block compare against the same
+    // partner bound (written a block earlier), so the block reads it once and
+    // passes it in (have_floor, floor_pre).
+    auto take = [&](float v, int step, int parity, bool have_floor = false,
+                    uint64_t floor_pre = 0ull) {
       const int j = jb + NS * step + stream;
       const bool ok = (step >= 0) & (j < myLe) & (((vmask >> (step & 63)) & 1ull) != 0ull);
       const uint64_t key = ok ? make_key(v, j) : 0ull;
       uint64_t bound = top.k[kHist - 1];
       if constexpr (NS == 2) {
-        const uint64_t floor = s_floor[parity ^ 1][stream ^ 1][tid];
+        const uint64_t floor = have_floor ? floor_pre : s_floor[parity ^ 1][stream ^ 1][tid];
         bound = floor > bound ? floor : bound;
         s_floor[parity][stream][tid] = top.k[kHist - 1];
       }
@@ -544,36 +547,38 @@ __global__ __launch_bounds__(64 * NS * (16 / CGW)) void prefill_score_kernel(
         // raised priority, so that the SIMD's other wave (in its selection
         // step) does not delay the next MFMA or load (about 1.7 % faster on
         // the mixed step in A/B).
-        // The block's first page's scale word and first operand tile are read
-        // together with the drain flags: stream 0's chain on that page then
+        // The block's first page's scale word and first operand tile, and the
+        // partner stream's bound for both selection steps, are read together
+        // with the drain flags: stream 0's chain on that page then
         // does not wait for a second LDS round trip after the check, and
         // stream 1's starts after its selection step and staging with them in
         // registers.
         const uint8_t *pg0 = s_page[stream][rb];
         const uint2 sc0 = *reinterpret_cast<const uint2 *>(pg0 + kLdsScales + 8 * lane);
         const u32x4 a00 = *reinterpret_cast<const u32x4 *>(pg0 + code_off);
+        const uint64_t fl = s_floor[parity ^ 1][stream ^ 1][tid];
         maybe_drain(parity);
         if (stream == 0) {
           __builtin_amdgcn_s_setprio(1);
           page_fold(rb, ma, true, sc0, a00);
           __builtin_amdgcn_s_setprio(0);
           pin(ma);
-          take(page_reduce(mb), k - 1, parity);
+          take(page_reduce(mb), k - 1, parity, true, fl);
           stage();
           __builtin_amdgcn_s_setprio(1);
           page_fold(rb + 1, mb);
           __builtin_amdgcn_s_setprio(0);
           pin(mb);
-          take(page_reduce(ma), k, parity);
+          take(page_reduce(ma), k, parity, true, fl);
         } else {
-          take(page_reduce(mb), k - 1, parity);
+          take(page_reduce(mb), k - 1, parity, true, fl);
           pin(mb);
           stage();
           __builtin_amdgcn_s_setprio(1);
           page_fold(rb, ma, true, sc0, a00);
           __builtin_amdgcn_s_setprio(0);
           pin(ma);
-          take(page_reduce(ma), k, parity);
+          take(page_reduce(ma), k, parity, true, fl);
           pin(ma);
           __builtin_amdgcn_s_setprio(1);
           page_fold(rb + 1, mb);
