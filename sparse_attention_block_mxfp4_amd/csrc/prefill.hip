@@ -4,8 +4,9 @@
 // query columns (column = row * H + head), 64 per wave, so each wave holds
 // four 16-column MFMA B operands in registers while it works on the tile.
 // The tile's causal pages 0..L_max-1 are walked in two interleaved page
-// streams of four waves each; each page (8704 bytes) is staged once into LDS
-// -- a ring of four buffers per stream, two pages per barrier, the next two
+// streams of four waves each; each page (8704 bytes) is staged once into LDS,
+// rearranged so that the MFMA operand reads are aligned and few (below) --
+// a ring of four buffers per stream, two pages per barrier, the next two
 // pages' global loads in flight while the current two are consumed -- and
 // re-read by the stream's four waves as the MFMA A operand.  At the end of a
 // walk the two streams' lists are merged in LDS.
