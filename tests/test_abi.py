@@ -300,13 +300,18 @@ def _plan_host(m, cu, sl, H, budget):
     return words, out.num_lists, out.num_chunks, out.num_merges
 
 
+# The planner's cost of a piece's set-up, in pages (its lists balance pages +
+# this per piece).
+PIECE_COST = 24
+
+
 def _check_plan(words, n_lists, n_chunks, n_merges, cu, sl, H, budget):
     """Every row in exactly one tile of M rows; each tile's pieces split its
     pages [0, pages) into consecutive ranges, with slots consecutive in page
     order and one merge record when split; work lists hold consecutive
     pieces and come in request order of their first piece; the chunk count
-    is the pages' greedy rule.  Returns the list costs (pages + 32 per
-    piece)."""
+    is the pages' greedy rule.  Returns the list costs (pages + PIECE_COST
+    per piece)."""
     qn = np.diff(cu)
     M = 256 // H
     assert words[0] == n_lists and words[1] == M and words[2] == H and words[3] == n_chunks
@@ -351,7 +356,7 @@ def _check_plan(words, n_lists, n_chunks, n_merges, cu, sl, H, budget):
     # a request's lists on neighbouring workgroups of one XCD)
     firsts = [int(pieces[f][0]) for f, _, _, _ in sorted(lists.tolist())]
     assert firsts == sorted(firsts)
-    return [int(sum(p[4] - p[3] + 32 for p in pieces[f:f + c])) for f, c, _, _ in lists]
+    return [int(sum(p[4] - p[3] + PIECE_COST for p in pieces[f:f + c])) for f, c, _, _ in lists]
 
 
 @pytest.mark.parametrize("H", [1, 3, 4, 8])
@@ -383,7 +388,8 @@ def test_prefill_work_lists_balance_ragged_rows(m, seed):
     words, n, ch, mg = _plan_host(m, cu, sl, 4, 1024)
     costs = _check_plan(words, n, ch, mg, cu, sl, 4, 1024)
     M = 64
-    tile_cost = [max((c + r0 + M - 1) // 128, 0) + 32 for c in ctx for r0 in range(0, 4096, M)]
+    tile_cost = [max((c + r0 + M - 1) // 128, 0) + PIECE_COST for c in ctx
+                 for r0 in range(0, 4096, M)]
     share = sum(tile_cost) / 256
     assert n <= 256 and max(costs) <= 1.10 * share
     assert mg > 0                       # the longest tiles exceed the share and are split
