@@ -393,7 +393,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
   MergeWaveSmem &sm = smem[wave];
   const int qi = c / H, h = c - qi * H;
   const int64_t T = (int64_t)r * query_len + qi;
-  const int p = seq_lens[r] - query_len + qi;
+  // The request's item range is read together with its length (one round
+  // trip, not two); it is used only for a row with a local page.
+  const int2 info = reinterpret_cast<const int2 *>(ws + kWsHeaderBytes)[r];
+  const int sl = seq_lens[r];
+  asm volatile("" :: "s"(info.x), "s"(info.y), "s"(sl));
+  const int p = sl - query_len + qi;
   const int L = local_page(p, max_pages);
   int32_t *dst = out + (T * H + h) * kTopk;
   if (L < 0) {   // a padding or refused row: every slot empty
@@ -401,7 +406,6 @@ __global__ __launch_bounds__(64 * kMergeWaves) void decode_merge_kernel(
     return;
   }
   const uint64_t *lists = reinterpret_cast<const uint64_t *>(ws + lists_offset(num_reqs));
-  const int2 info = reinterpret_cast<const int2 *>(ws + kWsHeaderBytes)[r];
   const int first = info.x, n = max(1, min(info.y, kMaxItemsPerReq));
   auto list_of = [&](int x) -> const u32x4 * {
     return reinterpret_cast<const u32x4 *>(lists + ((size_t)(first + x) * rows + c) * kListKeys);
