@@ -256,13 +256,13 @@ def test_invalid_page_ids_inside_a_history_are_skipped():
     assert prefill_error_bits(step) & 1 == 1
 
 
-def _full_size(name, pick):
+def _full_size(name, pick, seed=0):
     """Run a full-size workload in the benchmark's launch configuration; check
     the contract invariants on every row, and compare the rows ``pick(w,
     step)`` names -- a list of (request, rows of the request) -- with the
     oracle, computed on CPU worker processes."""
-    w = W.make_workload(name, 0)
-    _banner(f"full-size {name}: T={w.T} pages={w.num_blocks}")
+    w = W.make_workload(name, seed)
+    _banner(f"full-size {name} seed {seed}: T={w.T} pages={w.num_blocks}")
     out, _, _, dw, step = run_gpu(w)
     Ls = []
     if w.Rd:
@@ -324,9 +324,11 @@ def test_full_size_multi_token_decode():
 
 
 @pytest.mark.slow
-def test_full_size_ragged_prefill():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_full_size_ragged_prefill(seed):
     """Every request: its last whole row tile (the longest histories) and one
-    row of each of its tiles the plan split into page ranges."""
+    row of each of its tiles the plan split into page ranges.  Three seeds:
+    their context lengths give plans of 64, 128 and 101 split tiles."""
     def pick(w, step):
         splits = split_tiles(step)
         assert splits, "the ragged batch is expected to split tiles"
@@ -337,7 +339,7 @@ def test_full_size_ragged_prefill():
             rows |= {row0 + nrows // 2 for (rq, row0, nrows) in splits if rq == r - w.Rd}
             jobs.append((r, np.array(sorted(rows))))
         return jobs
-    _full_size("ragged_prefill", pick)
+    _full_size("ragged_prefill", pick, seed)
 
 
 @pytest.mark.slow
