@@ -321,8 +321,9 @@ def cpu_baseline(w, budget_s):
     (scoring + selection) until about a third of the time budget is spent,
     then blocks of 256 rows of the first prefill request until the rest is;
     pages are encoded before the clock starts.  Extrapolated to the step by
-    counts of requests and rows.  BLAS runs one thread per core this process
-    may use (its CPU affinity)."""
+    the count of decode requests, and for prefill by the history pages
+    decoded and the (row, page) pairs scored.  BLAS runs one thread per core
+    this process may use (its CPU affinity)."""
     from threadpoolctl import threadpool_limits
     cores = len(os.sched_getaffinity(0))
     with threadpool_limits(cores):
@@ -378,13 +379,22 @@ def _cpu_baseline(w, budget_s, cores):
             t_rows += time.perf_counter() - t0
             n += m
         sample_s += t_pages + t_rows
-        est += w.Rp * t_pages + t_rows * (w.n_prefill_rows / n)
+        # Extrapolated by work, not counts, since requests differ in length:
+        # page decoding by the history pages a request's rows reach, scoring
+        # by (row, page) pairs (a row scores its p // 128 history pages and
+        # its local page).
+        hist = [(int(c) + int(q) - 1) // 128 if q > 0 else 0 for c, q in zip(w.pre_ctx, w.pre_new)]
+        row_pages = sum(int(np.sum((int(c) + np.arange(int(q))) // 128 + 1))
+                        for c, q in zip(w.pre_ctx, w.pre_new))
+        est += (t_pages * sum(hist) / max(hist[0], 1)
+                + t_rows * row_pages / max(int(np.sum(pos_all[:n] // 128 + 1)), 1))
         parts.append(f"prefill request {r}: page decode + rows 0..{n - 1} of {new} x {w.H} "
                      f"heads over up to {int(pos_all[n - 1] // 128)} pages")
     return {"value": w.T / est if est > 0 else None, "unit": "query rows/s", "cores": int(cores),
             "kind": "oracle", "sample": "; ".join(parts) +
-            f"; {sample_s:.1f} s of oracle time, extrapolated to the step by request and row "
-            f"counts (est. {est:.1f} s per step)",
+            f"; {sample_s:.1f} s of oracle time, extrapolated to the step by decode requests "
+            f"and by prefill pages and (row, page) pairs (est. {est:.1f} s per step)",
+            "sample_seconds": round(sample_s, 4), "step_seconds_est": round(est, 4),
             "blas_threads": int(blas_threads), "affinity_cpus": int(cores),
             "host_cpus": os.cpu_count(), "cpu": _cpu_model()}
 

@@ -91,3 +91,27 @@ def test_timing_event_needs_a_device():
     import pytest
     with pytest.raises(RuntimeError):
         bench.TimingEvent()
+
+
+def test_cpu_baseline_extrapolates_by_work():
+    """The oracle's sample and its extrapolation: a decode-only workload small
+    enough to be sampled whole is not extrapolated (the estimate is the
+    sample's time), and a prefill-only one whose requests differ in length
+    is extrapolated by history pages and (row, page) pairs: between the
+    sample scaled by the smaller and by the larger of the two ratios."""
+    w = W.make_workload("decode_batch_small", 0)
+    cb = bench.cpu_baseline(w, budget_s=60.0)
+    assert cb["kind"] == "oracle" and cb["cores"] == len(os.sched_getaffinity(0))
+    assert f"decode requests 0..{w.Rd - 1} of {w.Rd}" in cb["sample"]
+    assert abs(cb["step_seconds_est"] - cb["sample_seconds"]) <= 1e-3
+    assert abs(w.T / cb["value"] - cb["step_seconds_est"]) <= 1e-3
+    w = W.make_workload("ragged_prefill_small", 0)
+    cb = bench.cpu_baseline(w, budget_s=60.0)
+    assert f"rows 0..{int(w.pre_new[0]) - 1} of {int(w.pre_new[0])}" in cb["sample"]
+    hist = [(int(c) + int(q) - 1) // 128 for c, q in zip(w.pre_ctx, w.pre_new)]
+    pairs = [int(np.sum((int(c) + np.arange(int(q))) // 128 + 1))
+             for c, q in zip(w.pre_ctx, w.pre_new)]
+    ratios = (sum(hist) / hist[0], sum(pairs) / pairs[0])
+    assert len(set(pairs)) > 1                  # the requests differ in work
+    est, sample = cb["step_seconds_est"], cb["sample_seconds"]
+    assert sample * min(ratios) - 1e-3 <= est <= sample * max(ratios) + 1e-3
