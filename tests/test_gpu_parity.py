@@ -310,9 +310,10 @@ def test_full_size_decode_batch():
 
 
 @pytest.mark.slow
-def test_full_size_multi_token_decode():
+@pytest.mark.parametrize("seed", [0, 1])
+def test_full_size_multi_token_decode(seed):
     """Every 8th request (16 of 128), all four query rows."""
-    w, out = _full_size("multi_token_decode", _decode_requests(range(0, 128, 8)))
+    w, out = _full_size("multi_token_decode", _decode_requests(range(seed, 128, 8)), seed)
     hits = total = 0
     for r in range(w.Rd):
         planted = set(w.planted_pages(r).tolist())
@@ -343,13 +344,14 @@ def test_full_size_ragged_prefill(seed):
 
 
 @pytest.mark.slow
-def test_full_size_mixed_step():
+@pytest.mark.parametrize("seed", [0, 1])
+def test_full_size_mixed_step(seed):
     """Every 4th decode request (8 of 32), both rows; a whole row tile of
     each prefill request (the last of the first, a middle one of the
-    second)."""
+    second; other tiles and requests for seed 1)."""
     def pick(w, step):
-        jobs = [(r, np.arange(w.query_len)) for r in range(0, w.Rd, 4)]
-        jobs.append((w.Rd, _prefill_tile(w, w.Rd, 8192 // 64 - 1)))
-        jobs.append((w.Rd + 1, _prefill_tile(w, w.Rd + 1, 64)))
+        jobs = [(r, np.arange(w.query_len)) for r in range(seed, w.Rd, 4)]
+        jobs.append((w.Rd, _prefill_tile(w, w.Rd, 8192 // 64 - 1 - 7 * seed)))
+        jobs.append((w.Rd + 1, _prefill_tile(w, w.Rd + 1, 64 + 13 * seed)))
         return jobs
-    _full_size("mixed_step", pick)
+    _full_size("mixed_step", pick, seed)
