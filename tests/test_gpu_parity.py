@@ -256,13 +256,13 @@ def test_invalid_page_ids_inside_a_history_are_skipped():
     assert prefill_error_bits(step) & 1 == 1
 
 
-def _full_size(name, pick, seed=0):
+def _full_size(name, pick, seed=0, q_dtype="e4m3"):
     """Run a full-size workload in the benchmark's launch configuration; check
     the contract invariants on every row, and compare the rows ``pick(w,
     step)`` names -- a list of (request, rows of the request) -- with the
     oracle, computed on CPU worker processes."""
-    w = W.make_workload(name, seed)
-    _banner(f"full-size {name} seed {seed}: T={w.T} pages={w.num_blocks}")
+    w = W.make_workload(name, seed, q_dtype=q_dtype)
+    _banner(f"full-size {name} seed {seed} {q_dtype}: T={w.T} pages={w.num_blocks}")
     out, _, _, dw, step = run_gpu(w)
     Ls = []
     if w.Rd:
@@ -325,11 +325,12 @@ def test_full_size_multi_token_decode(seed):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_full_size_ragged_prefill(seed):
+@pytest.mark.parametrize("seed,q_dtype", [(0, "e4m3"), (1, "e4m3"), (2, "e4m3"), (0, "bf16")])
+def test_full_size_ragged_prefill(seed, q_dtype):
     """Every request: its last whole row tile (the longest histories) and one
     row of each of its tiles the plan split into page ranges.  Three seeds:
-    their context lengths give plans of 64, 128 and 101 split tiles."""
+    their context lengths give plans of 64, 128 and 101 split tiles; seed 0
+    also with a bf16 index-Q (the bf16 scorer's work-list path)."""
     def pick(w, step):
         splits = split_tiles(step)
         assert splits, "the ragged batch is expected to split tiles"
@@ -340,7 +341,7 @@ def test_full_size_ragged_prefill(seed):
             rows |= {row0 + nrows // 2 for (rq, row0, nrows) in splits if rq == r - w.Rd}
             jobs.append((r, np.array(sorted(rows))))
         return jobs
-    _full_size("ragged_prefill", pick, seed)
+    _full_size("ragged_prefill", pick, seed, q_dtype)
 
 
 @pytest.mark.slow
