@@ -40,7 +40,7 @@ constexpr int kQueue = 16;              // per-column key queue (LDS)
 constexpr int kBufs = 4;                // LDS page buffers per stream
 constexpr int kMaxLists = 512;          // work lists (scorer workgroups) per plan
 constexpr int kPieceCost = 24;          // planning cost of a piece's set-up, in pages
-constexpr int kMinSplit = 16;           // fewest pages a split piece gets
+constexpr int kMinSplit = 4;            // fewest pages a split piece gets
 constexpr int kListKeys = 16;           // 15 keys + an empty slot: 128-byte lists
 constexpr int kMaxSlots = 2 * kMaxLists;   // partial lists (one per split piece)
 
